@@ -1,0 +1,152 @@
+"""ctypes wrapper for the CPU oracle (``oracle/oracle.c``) -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may
+import this module.  The product path (``graph_all_pairs_amd``) never does.
+
+Functions mirror the C library:
+  * ``fw_i32(m, k_end=None)`` / ``fw_f64(m, k_end=None)``: plain Floyd-Warshall
+    on a copy of the matrix (pivots 0 .. k_end-1), returned as a new array;
+  * ``sssp_rows_i32(w, inf, srcs)`` / ``sssp_rows_f64(w, inf, srcs)``:
+    Dijkstra from each listed source, one output row per source;
+  * ``apsp(m, inf)``: the full distance matrix of an int32 or float32 input
+    (float32 is widened exactly to binary64 and the result stays binary64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(out: str = LIB, src: str = SRC, extra: tuple = ()) -> str:
+    """Compile the oracle with gcc (OpenMP, -O2, no fast-math, no FMA)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-ffp-contract=off", "-fno-fast-math", *extra, src, "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = LIB):
+    global _lib
+    if path == LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(path)
+    lib = ctypes.CDLL(path)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_fw_i32.argtypes = [p, i64, i64, i64]
+    lib.oracle_fw_i32.restype = None
+    lib.oracle_fw_f64.argtypes = [p, i64, i64, i64]
+    lib.oracle_fw_f64.restype = None
+    lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
+    lib.oracle_sssp_i32.restype = ctypes.c_int
+    lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
+    lib.oracle_sssp_f64.restype = ctypes.c_int
+    lib.oracle_sssp_rows_i32.argtypes = [p, i64, i64, i32, p, i64, p, i64]
+    lib.oracle_sssp_rows_i32.restype = ctypes.c_int
+    lib.oracle_sssp_rows_f64.argtypes = [p, i64, i64, ctypes.c_double, p, i64, p, i64]
+    lib.oracle_sssp_rows_f64.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    if path == LIB:
+        _lib = lib
+    return lib
+
+
+class Oracle:
+    """Bound view of one oracle build (the default one, or a test's variant)."""
+
+    def __init__(self, path: str = LIB):
+        self.lib = load(path)
+
+    def set_threads(self, t: int) -> None:
+        self.lib.oracle_set_threads(int(t))
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    def fw_i32(self, m: np.ndarray, k_end: int | None = None) -> np.ndarray:
+        a = np.array(m, dtype=np.int32, order="C", copy=True)
+        n = a.shape[0]
+        ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
+        self.lib.oracle_fw_i32(a.ctypes.data, n, ld, n if k_end is None else int(k_end))
+        return a
+
+    def fw_f64(self, m: np.ndarray, k_end: int | None = None) -> np.ndarray:
+        a = np.array(m, dtype=np.float64, order="C", copy=True)
+        n = a.shape[0]
+        ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
+        self.lib.oracle_fw_f64(a.ctypes.data, n, ld, n if k_end is None else int(k_end))
+        return a
+
+    def sssp_rows_i32(self, w: np.ndarray, inf: int, srcs) -> np.ndarray:
+        a = np.ascontiguousarray(w, dtype=np.int32)
+        n, ld = a.shape[0], a.shape[1]
+        s = np.ascontiguousarray(np.asarray(srcs, dtype=np.int64))
+        out = np.empty((len(s), max(n, 1)), dtype=np.int32)
+        if len(s):
+            rc = self.lib.oracle_sssp_rows_i32(a.ctypes.data, n, ld, int(inf),
+                                               s.ctypes.data, len(s), out.ctypes.data,
+                                               out.shape[1])
+            if rc != 0:
+                raise ValueError("oracle_sssp_rows_i32 rejected its arguments")
+        return out[:, :n]
+
+    def sssp_rows_f64(self, w: np.ndarray, inf: float, srcs) -> np.ndarray:
+        a = np.ascontiguousarray(w, dtype=np.float64)
+        n, ld = a.shape[0], a.shape[1]
+        s = np.ascontiguousarray(np.asarray(srcs, dtype=np.int64))
+        out = np.empty((len(s), max(n, 1)), dtype=np.float64)
+        if len(s):
+            rc = self.lib.oracle_sssp_rows_f64(a.ctypes.data, n, ld, float(inf),
+                                               s.ctypes.data, len(s), out.ctypes.data,
+                                               out.shape[1])
+            if rc != 0:
+                raise ValueError("oracle_sssp_rows_f64 rejected its arguments")
+        return out[:, :n]
+
+    def apsp(self, m: np.ndarray) -> np.ndarray:
+        """Full distance matrix: int32 stays int32, float32 becomes float64."""
+        if m.dtype == np.int32:
+            return self.fw_i32(m)
+        return self.fw_f64(m.astype(np.float64))
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def fw_i32(m, k_end=None):
+    return default().fw_i32(m, k_end)
+
+
+def fw_f64(m, k_end=None):
+    return default().fw_f64(m, k_end)
+
+
+def sssp_rows_i32(w, inf, srcs):
+    return default().sssp_rows_i32(w, inf, srcs)
+
+
+def sssp_rows_f64(w, inf, srcs):
+    return default().sssp_rows_f64(w, inf, srcs)
+
+
+def apsp(m):
+    return default().apsp(m)

@@ -1,0 +1,194 @@
+/*
+ * CPU oracle for all-pairs shortest paths -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the bench's CPU-baseline leg load
+ * this library.  It is a plain, slow, obviously correct statement of what the
+ * GPU path must compute, and it shares no code, header or constant with it.
+ *
+ * What is computed.  For a weighted digraph given as a dense row-major matrix
+ * W (W[i][i] = 0, W[i][j] = edge weight, or the caller's "infinity" sentinel
+ * when there is no edge), the all-pairs shortest-path distance
+ *     delta(i, j) = min over directed paths i -> j of the sum of the weights,
+ * with delta(i, i) = 0 and delta(i, j) = inf when j is unreachable from i.
+ * Weights are non-negative, so a shortest simple path exists whenever j is
+ * reachable and the minimum is well defined.
+ *
+ * Two independent routes to delta are given:
+ *
+ *  1. oracle_fw_*: the textbook Floyd-Warshall recurrence
+ *        d(i,j) <- min(d(i,j), d(i,k) + d(k,j))   for k = 0, 1, ..., n-1
+ *     with k outermost.  This is the recurrence that the blocked algorithm on
+ *     the page "Katz and Kider" (thesis section 4.6; its Phase 1 runs
+ *     "standard Floyd-Warshall" on a block) reorganises into tiles; the
+ *     blocked form performs the same relaxations in another order and reaches
+ *     the same distances (section 4.6, "the parallel versions giving the same
+ *     values as the serial one" is the corresponding claim on the
+ *     "Loops into zones" page, section "What it does not change").
+ *     An optional k_end < n stops after the first k_end pivots, which exposes
+ *     the intermediate matrices of the recurrence to the tests.
+ *
+ *  2. oracle_sssp_*: Dijkstra's algorithm from one source, written the way the
+ *     Johnson's-algorithm page formalises it (Ukrainian/Russian CEUR paper on
+ *     Johnson's APSP with Glushkov algebras, operators init, ExtractMin and
+ *     RelaxEdge): all distances start at infinity except the source's 0; the
+ *     unsettled vertex with the smallest tentative distance is settled; each
+ *     of its out-edges (u,v) relaxes d(v) when d(v) > d(u) + w(u,v).
+ *     One call yields one row of delta, so sampled rows of very large
+ *     matrices can be checked without the cubic recurrence.
+ *
+ * Arithmetic.  int32 inputs: every candidate sum is formed in int64, so no
+ * overflow can occur whatever the sentinel.  Floating-point inputs are
+ * computed in binary64 (the caller widens float32 weights exactly); sums are
+ * single IEEE additions, min is exact, no fused or reassociated operations.
+ *
+ * Parallelism.  Within one pivot k, the rows i are independent: row k and
+ * column k do not change during step k because d(k,k) = 0 (or >= 0), so
+ * d(i,k) + d(k,k) >= d(i,k) and d(k,k) + d(k,j) >= d(k,j).  Each element
+ * therefore sees exactly the same sequence of operations whether the i loop
+ * runs serially or under OpenMP, and the results are bit-identical.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 0; /* 0 = OpenMP default */
+
+void oracle_set_threads(int t) { g_threads = t < 0 ? 0 : t; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+int oracle_version(void) { return 1; }
+
+/* Floyd-Warshall on int32 distances, in place; pivots k = 0 .. k_end-1. */
+void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {
+  if (k_end > n) k_end = n;
+  int nt = oracle_max_threads();
+  for (int64_t k = 0; k < k_end; ++k) {
+    const int32_t *row_k = d + k * ld;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t i = 0; i < n; ++i) {
+      int32_t *row_i = d + i * ld;
+      int64_t d_ik = row_i[k];
+      for (int64_t j = 0; j < n; ++j) {
+        int64_t cand = d_ik + (int64_t)row_k[j];
+        if (cand < row_i[j]) row_i[j] = (int32_t)cand;
+      }
+    }
+  }
+}
+
+/* Floyd-Warshall on binary64 distances, in place; pivots k = 0 .. k_end-1. */
+void oracle_fw_f64(double *d, int64_t n, int64_t ld, int64_t k_end) {
+  if (k_end > n) k_end = n;
+  int nt = oracle_max_threads();
+  for (int64_t k = 0; k < k_end; ++k) {
+    const double *row_k = d + k * ld;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t i = 0; i < n; ++i) {
+      double *row_i = d + i * ld;
+      double d_ik = row_i[k];
+      for (int64_t j = 0; j < n; ++j) {
+        double cand = d_ik + row_k[j];
+        if (cand < row_i[j]) row_i[j] = cand;
+      }
+    }
+  }
+}
+
+/*
+ * Dijkstra from `src` on the dense int32 weight matrix w (edge u->v exists
+ * when u != v and w[u][v] != inf).  Writes delta(src, .) to out[0..n-1]:
+ * unreachable vertices get exactly `inf`.  Returns 0, or -1 on bad arguments
+ * or allocation failure.
+ */
+int oracle_sssp_i32(const int32_t *w, int64_t n, int64_t ld, int32_t inf,
+                    int64_t src, int32_t *out) {
+  if (n <= 0 || src < 0 || src >= n) return -1;
+  int64_t *dist = (int64_t *)malloc((size_t)n * sizeof(int64_t));
+  unsigned char *settled = (unsigned char *)calloc((size_t)n, 1);
+  if (!dist || !settled) { free(dist); free(settled); return -1; }
+  for (int64_t v = 0; v < n; ++v) dist[v] = INT64_MAX; /* "infinity" */
+  dist[src] = 0;
+  for (;;) {
+    /* ExtractMin over the unsettled vertices with a finite distance. */
+    int64_t u = -1;
+    for (int64_t v = 0; v < n; ++v)
+      if (!settled[v] && dist[v] != INT64_MAX && (u < 0 || dist[v] < dist[u])) u = v;
+    if (u < 0) break;
+    settled[u] = 1;
+    const int32_t *wu = w + u * ld;
+    for (int64_t v = 0; v < n; ++v) { /* RelaxEdge(u, v) */
+      if (v == u || wu[v] == inf) continue;
+      int64_t cand = dist[u] + (int64_t)wu[v];
+      if (dist[v] > cand) dist[v] = cand;
+    }
+  }
+  for (int64_t v = 0; v < n; ++v)
+    out[v] = dist[v] == INT64_MAX ? inf : (int32_t)dist[v];
+  free(dist);
+  free(settled);
+  return 0;
+}
+
+/* Dijkstra from `src` on a dense binary64 weight matrix; see above. */
+int oracle_sssp_f64(const double *w, int64_t n, int64_t ld, double inf,
+                    int64_t src, double *out) {
+  if (n <= 0 || src < 0 || src >= n) return -1;
+  double *dist = (double *)malloc((size_t)n * sizeof(double));
+  unsigned char *reached = (unsigned char *)calloc((size_t)n, 1);
+  unsigned char *settled = (unsigned char *)calloc((size_t)n, 1);
+  if (!dist || !reached || !settled) {
+    free(dist); free(reached); free(settled); return -1;
+  }
+  dist[src] = 0.0;
+  reached[src] = 1;
+  for (;;) {
+    int64_t u = -1;
+    for (int64_t v = 0; v < n; ++v)
+      if (!settled[v] && reached[v] && (u < 0 || dist[v] < dist[u])) u = v;
+    if (u < 0) break;
+    settled[u] = 1;
+    const double *wu = w + u * ld;
+    for (int64_t v = 0; v < n; ++v) {
+      if (v == u || wu[v] == inf) continue;
+      double cand = dist[u] + wu[v];
+      if (!reached[v] || dist[v] > cand) { dist[v] = cand; reached[v] = 1; }
+    }
+  }
+  for (int64_t v = 0; v < n; ++v) out[v] = reached[v] ? dist[v] : inf;
+  free(dist);
+  free(reached);
+  free(settled);
+  return 0;
+}
+
+/* Many sources at once (each source independent; OpenMP over sources). */
+int oracle_sssp_rows_i32(const int32_t *w, int64_t n, int64_t ld, int32_t inf,
+                         const int64_t *srcs, int64_t nsrc, int32_t *out,
+                         int64_t ldo) {
+  int bad = 0;
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : bad)
+  for (int64_t s = 0; s < nsrc; ++s)
+    bad |= oracle_sssp_i32(w, n, ld, inf, srcs[s], out + s * ldo) != 0;
+  return bad ? -1 : 0;
+}
+
+int oracle_sssp_rows_f64(const double *w, int64_t n, int64_t ld, double inf,
+                         const int64_t *srcs, int64_t nsrc, double *out,
+                         int64_t ldo) {
+  int bad = 0;
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : bad)
+  for (int64_t s = 0; s < nsrc; ++s)
+    bad |= oracle_sssp_f64(w, n, ld, inf, srcs[s], out + s * ldo) != 0;
+  return bad ? -1 : 0;
+}

@@ -1,0 +1,91 @@
+"""Seeded input generator: determinism, shapes, distributions, padding."""
+import numpy as np
+import pytest
+
+import graphgen as gg
+
+
+def test_counter_rng_scalar_matches_vector():
+    c = np.arange(0, 1000, 37, dtype=np.uint64)
+    v = gg.u64_array(42, 3, c)
+    assert [gg.u64(42, 3, int(x)) for x in c] == [int(x) for x in v]
+
+
+def test_splitmix64_reference_values():
+    # SplitMix64 with state 0: the first outputs of the published generator
+    # (state += 0x9E3779B97F4A7C15, then the output mix).
+    z, out = 0, []
+    for _ in range(3):
+        z = (z + gg.GAMMA) & ((1 << 64) - 1)
+        out.append(gg.mix64(z))
+    assert out == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_same_seed_same_matrix_different_seed_differs():
+    a = gg.erdos_renyi(300, 0.1, 1, 100, 1)
+    b = gg.erdos_renyi(300, 0.1, 1, 100, 1)
+    c = gg.erdos_renyi(300, 0.1, 1, 100, 2)
+    assert gg.sha256_matrix(a) == gg.sha256_matrix(b) != gg.sha256_matrix(c)
+
+
+def test_er_density_and_weights():
+    n, p = 1000, 0.05
+    m = gg.erdos_renyi(n, p, 1, 1000, 2)
+    assert np.all(np.diag(m) == 0)
+    off = m[~np.eye(n, dtype=bool)]
+    edges = off[off != gg.INF_I32]
+    exp = p * n * (n - 1)
+    sd = np.sqrt(n * (n - 1) * p * (1 - p))
+    assert abs(len(edges) - exp) < 5 * sd
+    assert edges.min() >= 1 and edges.max() <= 1000
+    # roughly uniform: each decile holds ~10 %
+    h, _ = np.histogram(edges, bins=10, range=(0.5, 1000.5))
+    assert np.all(np.abs(h / len(edges) - 0.1) < 0.01)
+
+
+def test_complete_and_float():
+    m = gg.complete(200, 1, 10000, 3)
+    assert np.all(np.diag(m) == 0)
+    off = m[~np.eye(200, dtype=bool)]
+    assert off.min() >= 1 and off.max() <= 10000
+    f = gg.complete_f32(200, 5)
+    assert f.dtype == np.float32 and np.all(np.diag(f) == 0)
+    offf = f[~np.eye(200, dtype=bool)]
+    assert offf.min() >= np.float32(0.01) and offf.max() < 1.0
+
+
+def test_barabasi_albert_shape():
+    n, beta = 2000, 8
+    e = gg.barabasi_albert_edges(n, beta, 4)
+    assert len(e) == beta * (n - beta)
+    assert np.all(e[:, 0] > e[:, 1])                  # new vertex -> older vertex
+    for v in (beta + 1, 500, n - 1):                  # distinct targets
+        t = e[e[:, 0] == v, 1]
+        assert len(t) == beta and len(set(t.tolist())) == beta
+    m = gg.barabasi_albert(n, beta, 1, 255, 4)
+    assert np.array_equal(m, m.T)
+    assert (m != gg.INF_I32).sum() - n == 2 * beta * (n - beta)
+    deg = np.bincount(e.ravel(), minlength=n)
+    assert deg.max() > 10 * beta                       # heavy-tailed hubs
+
+
+@pytest.mark.parametrize("ld", [None, 64, 100])
+def test_padding_and_canary(ld):
+    m = gg.erdos_renyi(50, 0.2, 1, 9, 7, ld=ld, canary=-5)
+    assert m.shape == (50, ld or 50)
+    if ld:
+        assert np.all(m[:, 50:] == -5)
+    ref = gg.erdos_renyi(50, 0.2, 1, 9, 7)
+    assert np.array_equal(m[:, :50], ref)
+
+
+def test_workload_table_names():
+    assert set(gg.WORKLOADS) == {"er-256-p0.1-i32", "er-2048-p0.05-i32", "complete-8192-i32",
+                                 "ba-16000-b8-i32", "complete-12288-f32"}
+    m = gg.make_workload("er-256-p0.1-i32")
+    assert m.shape == (256, 256) and m.dtype == np.int32
+
+
+def test_zero_size():
+    m = gg.erdos_renyi(0, 0.5, 1, 9, 1, ld=4)
+    assert m.shape == (0, 4)

@@ -1,0 +1,102 @@
+"""The oracle's pins must be strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (a dropped
+term, a wrong sign, a transposed operand, a wrong index, a skipped pivot, a
+wrong extraction order), builds the copy on the CPU, and runs a compact
+battery of the same pins used in test_oracle_pins.py against it.  The battery
+must fail for every mutant and pass for the unmodified source.
+"""
+import numpy as np
+import pytest
+import scipy.sparse.csgraph as csg
+
+import graphgen as gg
+import oracle
+from _helpers import brute_force_apsp, random_small_graph, read_golden
+
+INF = gg.INF_I32
+
+MUTANTS = {
+    # Floyd-Warshall, int32
+    "fw_transposed_dik": ("int64_t d_ik = row_i[k];", "int64_t d_ik = d[k * ld + i];"),
+    "fw_wrong_index_dkj": ("int64_t cand = d_ik + (int64_t)row_k[j];",
+                           "int64_t cand = d_ik + (int64_t)row_k[i];"),
+    "fw_dropped_term": ("int64_t cand = d_ik + (int64_t)row_k[j];",
+                        "int64_t cand = (int64_t)row_k[j];"),
+    "fw_row_i_for_row_k": ("int64_t cand = d_ik + (int64_t)row_k[j];",
+                           "int64_t cand = d_ik + (int64_t)row_i[j];"),
+    "fw_max_not_min": ("if (cand < row_i[j]) row_i[j] = (int32_t)cand;",
+                       "if (cand > row_i[j]) row_i[j] = (int32_t)cand;"),
+    "fw_skips_first_pivot": ("for (int64_t k = 0; k < k_end; ++k) {\n    const int32_t",
+                             "for (int64_t k = 1; k < k_end; ++k) {\n    const int32_t"),
+    "fw_skips_last_pivot": ("void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {\n  if (k_end > n) k_end = n;",
+                            "void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {\n  if (k_end > n - 1) k_end = n - 1;"),
+    "fw_diagonal_only_rows": ("for (int64_t i = 0; i < n; ++i) {\n      int32_t *row_i",
+                              "for (int64_t i = 0; i < n; i += 2) {\n      int32_t *row_i"),
+    # Floyd-Warshall, binary64
+    "fw64_max_not_min": ("if (cand < row_i[j]) row_i[j] = cand;",
+                         "if (cand > row_i[j]) row_i[j] = cand;"),
+    "fw64_transposed_dik": ("double d_ik = row_i[k];", "double d_ik = d[k * ld + i];"),
+    # Dijkstra, int32
+    "sssp_extracts_max": ("(u < 0 || dist[v] < dist[u])) u = v;\n    if (u < 0) break;\n    settled[u] = 1;\n    const int32_t",
+                          "(u < 0 || dist[v] > dist[u])) u = v;\n    if (u < 0) break;\n    settled[u] = 1;\n    const int32_t"),
+    "sssp_transposed_edge": ("const int32_t *wu = w + u * ld;\n    for (int64_t v = 0; v < n; ++v) { /* RelaxEdge(u, v) */\n      if (v == u || wu[v] == inf) continue;\n      int64_t cand = dist[u] + (int64_t)wu[v];",
+                             "const int32_t *wu = w + u * ld;\n    for (int64_t v = 0; v < n; ++v) { /* RelaxEdge(u, v) */\n      if (v == u || w[v * ld + u] == inf) continue;\n      int64_t cand = dist[u] + (int64_t)w[v * ld + u];"),
+    "sssp_dropped_dist_u": ("int64_t cand = dist[u] + (int64_t)wu[v];", "int64_t cand = (int64_t)wu[v];"),
+}
+
+
+def _battery(o: oracle.Oracle) -> None:
+    g = read_golden("hand4_fw.txt", INF)
+    w4 = g["input"].astype(np.int32)
+    for k_end, key in [(1, "after_k 1"), (2, "after_k 2"), (3, "after_k 3"), (4, "final")]:
+        assert np.array_equal(o.fw_i32(w4, k_end=k_end), g[key])
+    assert np.array_equal(o.sssp_rows_i32(w4, INF, range(4)), g["final"])
+    gf = read_golden("hand4_fw.txt", np.inf)
+    assert np.array_equal(o.fw_f64(gf["input"].astype(np.float64)), gf["final"].astype(np.float64))
+    for seed in range(40):
+        rng = np.random.default_rng(77 + seed)
+        n = int(rng.integers(2, 8))
+        w = random_small_graph(rng, n, 0.4, 9, INF)
+        want = brute_force_apsp(w, INF).astype(np.int64)
+        assert np.array_equal(o.fw_i32(w).astype(np.int64), want)
+        assert np.array_equal(o.sssp_rows_i32(w, INF, range(n)).astype(np.int64), want)
+        wf = random_small_graph(rng, n, 0.4, 4, np.inf, floats=True)
+        wantf = brute_force_apsp(wf, np.inf).astype(np.float64)
+        gotf = o.fw_f64(wf)
+        assert np.array_equal(np.isinf(gotf), np.isinf(wantf))
+        fin = np.isfinite(wantf)
+        assert np.allclose(gotf[fin], wantf[fin], rtol=1e-12)
+    n = 33
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    assert np.array_equal(o.fw_i32(gg.ring(n, 3)), 3 * ((j - i) % n))
+    w = gg.erdos_renyi(60, 0.08, 1, 20, 3)
+    ref = csg.shortest_path(csg.csgraph_from_dense(w.astype(np.float64), null_value=float(INF)),
+                            method="D")
+    ref = np.where(np.isinf(ref), INF, ref).astype(np.int64)
+    assert np.array_equal(o.fw_i32(w).astype(np.int64), ref)
+    assert np.array_equal(o.sssp_rows_i32(w, INF, range(60)).astype(np.int64), ref)
+
+
+def _build_variant(tmp_path, name, edit):
+    src = open(oracle.SRC).read()
+    if edit is not None:
+        old, new = edit
+        assert src.count(old) >= 1, f"mutant {name}: anchor text not found"
+        src = src.replace(old, new, 1)
+    p = tmp_path / f"{name}.c"
+    p.write_text(src)
+    out = tmp_path / f"lib{name}.so"
+    oracle.build(str(out), str(p))
+    return oracle.Oracle(str(out))
+
+
+def test_battery_passes_on_unmodified_oracle(tmp_path):
+    _battery(_build_variant(tmp_path, "pristine", None))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_battery_catches_mutant(tmp_path, name):
+    o = _build_variant(tmp_path, name, MUTANTS[name])
+    with pytest.raises(AssertionError):
+        _battery(o)

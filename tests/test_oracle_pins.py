@@ -1,0 +1,221 @@
+"""Pins for the CPU oracle: checks that do not rest on the oracle itself.
+
+Each test ties the oracle to something fixed from outside it:
+  * a hand-worked example (tests/golden/hand4_fw.txt), step by step;
+  * the literal definition (minimum over all simple paths) on tiny graphs;
+  * library routines (scipy's Dijkstra and Johnson implementations);
+  * closed forms (rings, paths, grids, complete graphs, disjoint rings);
+  * invariants (zero diagonal, triangle inequality, d <= W, symmetry on
+    undirected inputs, inf exactly on unreachable pairs, Bellman optimality);
+  * serial == multi-threaded bit for bit.
+"""
+import numpy as np
+import pytest
+import scipy.sparse.csgraph as csg
+
+import graphgen as gg
+from _helpers import (bellman_rows_ok, brute_force_apsp, random_small_graph,
+                      reachability, read_golden, triangle_ok)
+
+INF = gg.INF_I32
+
+
+# ---- hand-worked example -------------------------------------------------
+
+def test_hand_example_every_pivot(orc):
+    g = read_golden("hand4_fw.txt", INF)
+    w = g["input"].astype(np.int32)
+    for k_end, key in [(0, "input"), (1, "after_k 1"), (2, "after_k 2"),
+                       (3, "after_k 3"), (4, "final")]:
+        got = orc.fw_i32(w, k_end=k_end)
+        assert np.array_equal(got, g[key]), key
+
+
+def test_hand_example_f64_with_ieee_inf(orc):
+    g = read_golden("hand4_fw.txt", np.inf)
+    got = orc.fw_f64(g["input"].astype(np.float64))
+    assert np.array_equal(got, g["final"].astype(np.float64))
+
+
+def test_hand_example_dijkstra_rows(orc):
+    g = read_golden("hand4_fw.txt", INF)
+    w = g["input"].astype(np.int32)
+    assert np.array_equal(orc.sssp_rows_i32(w, INF, range(4)), g["final"])
+
+
+# ---- the definition, evaluated literally ---------------------------------
+
+@pytest.mark.parametrize("seed", range(240))
+def test_brute_force_small_int(orc, seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(1, 8))
+    p = [0.15, 0.35, 0.6, 0.9][seed % 4]
+    w = random_small_graph(rng, n, p, wmax=9, inf=INF)  # zero weights allowed
+    want = brute_force_apsp(w, INF).astype(np.int64)
+    assert np.array_equal(orc.fw_i32(w).astype(np.int64), want)
+    assert np.array_equal(orc.sssp_rows_i32(w, INF, range(n)).astype(np.int64), want)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_brute_force_small_float(orc, seed):
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(2, 8))
+    w = random_small_graph(rng, n, 0.5, wmax=4, inf=np.inf, floats=True)
+    want = brute_force_apsp(w, np.inf).astype(np.float64)
+    got = orc.fw_f64(w)
+    # path sums associate differently in FW and in the enumeration
+    assert np.array_equal(np.isinf(got), np.isinf(want))
+    fin = np.isfinite(want)
+    assert np.allclose(got[fin], want[fin], rtol=1e-12, atol=0)
+    got_d = orc.sssp_rows_f64(w, np.inf, range(n))
+    assert np.array_equal(np.isinf(got_d), np.isinf(want))
+    assert np.allclose(got_d[fin], want[fin], rtol=1e-12, atol=0)
+
+
+# ---- library routines ----------------------------------------------------
+
+def _scipy_apsp(w, inf, method):
+    g = csg.csgraph_from_dense(w.astype(np.float64), null_value=float(inf))
+    # csgraph_from_dense drops diagonal zeros only; explicit zero-weight
+    # off-diagonal edges are kept because null_value is the sentinel.
+    return csg.shortest_path(g, method=method, directed=True)
+
+
+@pytest.mark.parametrize("n,p,seed", [(50, 0.1, 1), (200, 0.03, 2), (333, 0.02, 3), (257, 0.5, 4)])
+def test_matches_scipy_dijkstra_and_johnson(orc, n, p, seed):
+    w = gg.erdos_renyi(n, p, 0, 50, seed)  # includes zero-weight edges
+    d = orc.fw_i32(w)
+    for method in ("D", "J"):
+        ref = _scipy_apsp(w, INF, method)
+        ref = np.where(np.isinf(ref), INF, ref).astype(np.int64)
+        assert np.array_equal(d.astype(np.int64), ref), method
+    rows = orc.sssp_rows_i32(w, INF, range(n))
+    assert np.array_equal(rows, d)
+
+
+def test_float_matches_scipy(orc):
+    w = gg.complete_f32(300, seed=9).astype(np.float64)
+    d = orc.fw_f64(w)
+    ref = _scipy_apsp(w, np.inf, "D")
+    assert np.allclose(d, ref, rtol=1e-13, atol=0)
+
+
+def test_zero_weight_edges_are_edges(orc):
+    # 0 -> 1 (weight 0) -> 2 (weight 0): d(0,2) must be 0, and scipy agrees
+    w = np.full((3, 3), INF, dtype=np.int32)
+    np.fill_diagonal(w, 0)
+    w[0, 1] = 0
+    w[1, 2] = 0
+    d = orc.fw_i32(w)
+    assert d[0, 2] == 0 and d[2, 0] == INF
+    ref = _scipy_apsp(w, INF, "D")
+    assert ref[0, 2] == 0 and np.isinf(ref[2, 0])
+
+
+# ---- closed forms ----------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 64, 65, 130])
+def test_directed_ring(orc, n):
+    w = 3
+    d = orc.fw_i32(gg.ring(n, w))
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    assert np.array_equal(d, w * ((j - i) % n))
+    dr = orc.fw_i32(gg.ring(n, w, reverse=True))
+    assert np.array_equal(dr, w * ((i - j) % n))
+
+
+def test_undirected_ring(orc):
+    n = 41
+    d = orc.fw_i32(gg.ring(n, 2, directed=False))
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    k = (j - i) % n
+    assert np.array_equal(d, 2 * np.minimum(k, n - k))
+
+
+def test_path_grid_complete_edgeless(orc):
+    n = 37
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    assert np.array_equal(orc.fw_i32(gg.undirected_path(n, 5)), 5 * np.abs(i - j))
+    r, c = 6, 9
+    d = orc.fw_i32(gg.grid(r, c))
+    v = np.arange(r * c)
+    man = np.abs(v[:, None] // c - v[None, :] // c) + np.abs(v[:, None] % c - v[None, :] % c)
+    assert np.array_equal(d, man)
+    ce = orc.fw_i32(gg.complete_equal(n, 7))
+    assert np.array_equal(ce, np.where(i == j, 0, 7))
+    e = gg.edgeless(n)
+    assert np.array_equal(orc.fw_i32(e), e)
+
+
+def test_two_rings_keep_inf_between_components(orc):
+    n1, n2 = 13, 20
+    d = orc.fw_i32(gg.two_rings(n1, n2, 4))
+    assert np.all(d[:n1, n1:] == INF) and np.all(d[n1:, :n1] == INF)
+    i, j = np.meshgrid(np.arange(n2), np.arange(n2), indexing="ij")
+    assert np.array_equal(d[n1:, n1:], 4 * ((j - i) % n2))
+
+
+def test_float_closed_forms_are_exact(orc):
+    n = 50
+    d = orc.fw_f64(gg.ring(n, 0.5, dtype=np.float64, inf=np.inf))
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    assert np.array_equal(d, 0.5 * ((j - i) % n))
+    d2 = orc.fw_f64(gg.two_rings(7, 9, 0.25, dtype=np.float64, inf=np.inf))
+    assert np.all(np.isinf(d2[:7, 7:]))
+
+
+# ---- invariants ------------------------------------------------------------
+
+@pytest.mark.parametrize("n,p,seed", [(120, 0.03, 11), (97, 0.2, 12), (160, 0.01, 13)])
+def test_invariants_random(orc, n, p, seed):
+    w = gg.erdos_renyi(n, p, 1, 30, seed)
+    d = orc.fw_i32(w)
+    assert np.all(np.diag(d) == 0)
+    assert np.all(d <= w)
+    assert triangle_ok(d)
+    reach = reachability(w, INF)
+    assert np.array_equal(d == INF, ~reach)
+    assert bellman_rows_ok(w, d, range(n), INF)
+
+
+def test_undirected_input_gives_symmetric_output(orc):
+    w = gg.barabasi_albert(300, 3, 1, 255, seed=21)
+    d = orc.fw_i32(w)
+    assert np.array_equal(d, d.T)
+    assert triangle_ok(d)
+
+
+def test_padding_columns_untouched(orc):
+    n, ld = 45, 64
+    w = gg.erdos_renyi(n, 0.1, 1, 9, 5, ld=ld, canary=-7)
+    d = orc.fw_i32(w)
+    assert np.all(d[:, n:] == -7)
+    assert np.array_equal(d[:, :n], orc.fw_i32(np.ascontiguousarray(w[:, :n])))
+
+
+# ---- threading -------------------------------------------------------------
+
+def test_serial_equals_parallel(orc):
+    w = gg.erdos_renyi(300, 0.05, 1, 100, 31)
+    wf = gg.complete_f32(300, 32).astype(np.float64)
+    orc.set_threads(1)
+    try:
+        a, af = orc.fw_i32(w), orc.fw_f64(wf)
+    finally:
+        orc.set_threads(0)
+    orc.set_threads(8)
+    try:
+        b, bf = orc.fw_i32(w), orc.fw_f64(wf)
+    finally:
+        orc.set_threads(0)
+    assert np.array_equal(a, b)
+    assert np.array_equal(af.view(np.int64), bf.view(np.int64))
+
+
+def test_dijkstra_rows_match_fw_on_workload_shapes(orc):
+    # the two oracle routes agree on the workload families at reduced size
+    for w in (gg.erdos_renyi(512, 0.05, 1, 1000, 2), gg.complete(384, 1, 10000, 3),
+              gg.barabasi_albert(600, 8, 1, 255, 4)):
+        d = orc.fw_i32(w)
+        src = np.arange(0, w.shape[0], 7)
+        assert np.array_equal(orc.sssp_rows_i32(w, INF, src), d[src])
