@@ -1,0 +1,201 @@
+"""Python binding of the gfx950 blocked Floyd-Warshall library (libapsp.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/apsp.h.  PyTorch is used for
+device memory and streams; nothing here computes distances, and there is no
+CPU fallback -- a missing library raises.
+
+Raw entry points (same names and arguments as the C ABI; pointers and
+streams are integers):
+    apsp_fw_i32(d_ptr, n, ld, inf, stream) -> status
+    apsp_fw_f32(d_ptr, n, ld, inf, stream) -> status
+    apsp_fw_rounds_i32(d_ptr, n, ld, inf, r0, r1, stream) -> status
+    apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream) -> status
+    apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, phase_ms[3], launches[3])
+    apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, phase_ms[3], launches[3])
+    apsp_pivot_block(n), apsp_status_string(s), apsp_last_hip_error(), apsp_version()
+
+Tensor convenience:
+    fw(t, inf=None)              in-place APSP of a 2-D int32/float32 CUDA tensor
+    fw_rounds(t, r0, r1, inf=None)
+    fw_timed(t, inf=None)        -> (phase_ms, launches), synchronised
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB_PATH
+
+APSP_OK = 0
+APSP_ERR_INVALID_VALUE = 1
+APSP_ERR_NO_DEVICE = 2
+APSP_ERR_LAUNCH = 3
+
+INF_I32 = 0x3FFFFFFF
+
+# Every symbol that include/apsp.h declares.
+EXPORTS = (
+    "apsp_fw_i32", "apsp_fw_f32", "apsp_fw_rounds_i32", "apsp_fw_rounds_f32",
+    "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_pivot_block",
+    "apsp_status_string", "apsp_last_hip_error", "apsp_version",
+)
+
+_lib = None
+
+
+class APSPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {apsp_status_string(status)}"
+        if status == APSP_ERR_LAUNCH:
+            msg += f" (hipError {apsp_last_hip_error()})"
+        super().__init__(msg)
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load(path: str | None = None):
+    """Load libapsp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    # torch ships its own HIP runtime whose SONAME matches the one libapsp.so
+    # links against; importing torch first makes the dynamic linker bind
+    # libapsp.so to that already-loaded runtime, so device pointers and
+    # streams from torch are valid inside the library (one runtime only).
+    import torch  # noqa: F401
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no fallback")
+    lib = ctypes.CDLL(p)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    dp, lp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "apsp_fw_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_fw_f32": ([vp, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_fw_rounds_i32": ([vp, i64, i64, i32, i64, i64, vp], ctypes.c_int),
+        "apsp_fw_rounds_f32": ([vp, i64, i64, f32, i64, i64, vp], ctypes.c_int),
+        "apsp_fw_timed_i32": ([vp, i64, i64, i32, vp, dp, lp], ctypes.c_int),
+        "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp], ctypes.c_int),
+        "apsp_pivot_block": ([i64], i64),
+        "apsp_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "apsp_last_hip_error": ([], ctypes.c_int),
+        "apsp_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+# ---- raw C-ABI mirrors ------------------------------------------------------
+
+def apsp_fw_i32(d_ptr: int, n: int, ld: int, inf: int, stream: int = 0) -> int:
+    return load().apsp_fw_i32(d_ptr or None, n, ld, inf, stream or None)
+
+
+def apsp_fw_f32(d_ptr: int, n: int, ld: int, inf: float, stream: int = 0) -> int:
+    return load().apsp_fw_f32(d_ptr or None, n, ld, inf, stream or None)
+
+
+def apsp_fw_rounds_i32(d_ptr, n, ld, inf, r0, r1, stream=0) -> int:
+    return load().apsp_fw_rounds_i32(d_ptr or None, n, ld, inf, r0, r1, stream or None)
+
+
+def apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream=0) -> int:
+    return load().apsp_fw_rounds_f32(d_ptr or None, n, ld, inf, r0, r1, stream or None)
+
+
+def _timed(fn, d_ptr, n, ld, inf, stream):
+    ms = (ctypes.c_double * 3)()
+    cnt = (ctypes.c_int64 * 3)()
+    st = fn(d_ptr or None, n, ld, inf, stream or None, ms, cnt)
+    return st, list(ms), list(cnt)
+
+
+def apsp_fw_timed_i32(d_ptr, n, ld, inf, stream=0):
+    return _timed(load().apsp_fw_timed_i32, d_ptr, n, ld, inf, stream)
+
+
+def apsp_fw_timed_f32(d_ptr, n, ld, inf, stream=0):
+    return _timed(load().apsp_fw_timed_f32, d_ptr, n, ld, inf, stream)
+
+
+def apsp_pivot_block(n: int = 0) -> int:
+    return int(load().apsp_pivot_block(n))
+
+
+def apsp_status_string(status: int) -> str:
+    return load().apsp_status_string(status).decode()
+
+
+def apsp_last_hip_error() -> int:
+    return int(load().apsp_last_hip_error())
+
+
+def apsp_version() -> int:
+    return int(load().apsp_version())
+
+
+# ---- tensor convenience -----------------------------------------------------
+
+def _tensor_args(t, inf):
+    import torch
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    n = t.shape[0]
+    if t.shape[1] < n:
+        raise ValueError("expected at least n columns")
+    if t.stride(1) != 1 and t.shape[1] > 1:
+        raise ValueError("tensor rows must be contiguous (stride(1) == 1)")
+    ld = max(t.stride(0), t.shape[1], 1) if n <= 1 else t.stride(0)
+    if t.dtype == torch.int32:
+        kind = "i32"
+        inf = INF_I32 if inf is None else int(inf)
+    elif t.dtype == torch.float32:
+        kind = "f32"
+        inf = float("inf") if inf is None else float(inf)
+    else:
+        raise ValueError("dtype must be int32 or float32")
+    stream = torch.cuda.current_stream(t.device).cuda_stream
+    return kind, t.data_ptr(), n, ld, inf, stream
+
+
+def fw(t, inf=None):
+    """In-place APSP of t[:n, :n] (n = t.shape[0]) on the current stream."""
+    import torch
+    kind, p, n, ld, inf, s = _tensor_args(t, inf)
+    with torch.cuda.device(t.device):
+        st = (apsp_fw_i32 if kind == "i32" else apsp_fw_f32)(p, n, ld, inf, s)
+    if st != APSP_OK:
+        raise APSPError(st, "apsp_fw_" + kind)
+    return t
+
+
+def fw_rounds(t, r0, r1, inf=None):
+    import torch
+    kind, p, n, ld, inf, s = _tensor_args(t, inf)
+    with torch.cuda.device(t.device):
+        st = (apsp_fw_rounds_i32 if kind == "i32" else apsp_fw_rounds_f32)(p, n, ld, inf, r0, r1, s)
+    if st != APSP_OK:
+        raise APSPError(st, "apsp_fw_rounds_" + kind)
+    return t
+
+
+def fw_timed(t, inf=None):
+    import torch
+    kind, p, n, ld, inf, s = _tensor_args(t, inf)
+    with torch.cuda.device(t.device):
+        st, ms, cnt = (apsp_fw_timed_i32 if kind == "i32" else apsp_fw_timed_f32)(p, n, ld, inf, s)
+    if st != APSP_OK:
+        raise APSPError(st, "apsp_fw_timed_" + kind)
+    return ms, cnt

@@ -1,0 +1,635 @@
+// Blocked Floyd-Warshall all-pairs shortest paths for gfx950 (MI355X).
+//
+// Method: the blocked Floyd-Warshall of the page "Katz and Kider" (thesis
+// section 4.6, Algorithms 16-18, Figures 4.2-4.5).  The n x n distance matrix
+// is cut into B x B pivot blocks; round K
+//   Phase 1  closes the diagonal block D_KK (Floyd-Warshall inside the block);
+//   Phase 2  updates the pivot-row blocks D_KJ and pivot-column blocks D_IK;
+//   Phase 3  updates every other block D_IJ from D_IK and D_KJ;
+// and the next round takes the next diagonal block.
+//
+// gfx950 design (what differs from the page's 16 x 16 CUDA design):
+//  * B = 128.  Phase 3 gives each 256-thread workgroup a 128 x 128 output tile
+//    held in registers as an 8 x 8 micro-tile per thread; the 128 x 128 pivot
+//    column/row operands stream through LDS in k-chunks, double buffered, the
+//    column operand stored k-major so that every operand fetch is a 128-bit
+//    LDS read with no bank conflict.  Per pair of pivots each output costs two
+//    adds and one three-input min (v_add_u32 / v_add_f32 + v_min3).
+//  * Phase 2 is computed with the closed diagonal block:
+//      D_KJ <- min(D_KJ, D_KK* (x) D_KJ),   D_IK <- min(D_IK, D_IK (x) D_KK*),
+//    where (x) is the min-plus product.  Both sides equal the shortest
+//    distances through intermediates in blocks <= K, so this is the same
+//    result as the page's in-place pivot loop (exact for integers), and it
+//    turns Phase 2 into the same barrier-free product kernel as Phase 3.  Each
+//    Phase-2 workgroup owns all B rows (row panel) or all B columns (column
+//    panel) of its tile, so the operand it reads from its own tile is never
+//    written by another workgroup.
+//  * Phase 1 runs in one 1024-thread workgroup with the block in registers
+//    (4 x 4 per thread); only pivot row t and pivot column t travel through
+//    LDS, in ping-pong buffers, with one barrier per pivot.
+//  * Ragged n: rows and columns >= n behave as isolated vertices -- loads
+//    return inf, stores are suppressed -- so nothing outside the leading
+//    n x n block is read or written.
+//  * The page's skipPrimaryBlock equations (Figures 4.2, 4.3) become the index
+//    map j' -> j' + (j' >= K) on the workgroup id.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "apsp.h"
+
+namespace {
+
+constexpr int kB = 128;        // pivot block edge
+constexpr int kThreads = 256;  // Phase 2/3 workgroup size
+constexpr int kKC = 16;        // pivots per LDS chunk
+constexpr int kPad = 4;        // LDS row padding (elements), keeps 16-B alignment
+constexpr int kWavesP3 = 2;    // waves per SIMD targeted by Phase 3 (<= 256 VGPRs)
+constexpr int kWavesP2 = 4;    // waves per SIMD targeted by Phase 2 (<= 128 VGPRs)
+
+// ---------------------------------------------------------------------------
+// Element operations.  int32: wrap-free because every value is <= inf <=
+// 2^30 - 1.  float32: IEEE add and min (no NaN by precondition).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t mp_min(int32_t a, int32_t b) { return min(a, b); }
+__device__ __forceinline__ float mp_min(float a, float b) { return fminf(a, b); }
+
+// min(a, b, c) as one v_min3.  Written as an instruction so that the compiler
+// keeps one three-input min per pair of candidates instead of re-balancing
+// the chain into two-input mins.
+__device__ __forceinline__ int32_t mp_min3(int32_t a, int32_t b, int32_t c) {
+  int32_t r;
+  asm("v_min3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float mp_min3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <typename T> struct Vec4;
+template <> struct Vec4<int32_t> { using type = int4; };
+template <> struct Vec4<float> { using type = float4; };
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* __restrict__ p, T (&v)[4]) {
+  using V = typename Vec4<T>::type;
+  V x = *reinterpret_cast<const V*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* __restrict__ p, const T (&v)[4]) {
+  using V = typename Vec4<T>::type;
+  V x; x.x = v[0]; x.y = v[1]; x.z = v[2]; x.w = v[3];
+  *reinterpret_cast<V*>(p) = x;
+}
+
+// Four consecutive elements of row `row`, columns col .. col+3, of the
+// matrix; out-of-range elements read as inf.  VEC: one 128-bit load when the
+// whole quad is in range.  EDGE=false promises the quad is in range.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void gload4(const T* __restrict__ d, int64_t ld, int64_t n,
+                                       int64_t row, int64_t col, T inf, T (&v)[4]) {
+  const T* p = d + row * ld + col;
+  if (!EDGE) {
+    if (VEC) { load4(p, v); }
+    else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = p[e];
+    }
+  } else {
+    if (row < n && col + 3 < n) {
+      if (VEC) { load4(p, v); }
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = p[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (row < n && col + e < n) ? p[e] : inf;
+    }
+  }
+}
+
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void gstore4(T* __restrict__ d, int64_t ld, int64_t n,
+                                        int64_t row, int64_t col, const T (&v)[4]) {
+  T* p = d + row * ld + col;
+  if (!EDGE) {
+    if (VEC) { store4(p, v); }
+    else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = v[e];
+    }
+  } else {
+    if (row < n && col + 3 < n) {
+      if (VEC) { store4(p, v); }
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = v[e];
+      }
+    } else if (row < n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < n) p[e] = v[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Min-plus tile update  C <- min(C, A (x) B)  for one workgroup.
+//   C = D[row0 .. row0+TM) x [col0 .. col0+TN)
+//   A = D[row0 .. row0+TM) x [kb0 .. kb0+kB)      (pivot columns)
+//   B = D[kb0 .. kb0+kB)  x [col0 .. col0+TN)     (pivot rows)
+// Thread layout: (TM/RM) x (TN/RN) = 256 threads, each holding an RM x RN
+// micro-tile made of (RM/4) x (RN/4) blocks of 4 x 4 spaced TM/(RM/4) rows
+// and TN/(RN/4) columns apart.  The C tile stays in registers for the whole
+// kB-deep update and is written once at the end, so a tile may alias A or B.
+// ---------------------------------------------------------------------------
+template <typename T, int TM, int TN, int RM, int RN>
+struct TileShape {
+  static constexpr int kThrCols = TN / RN;
+  static constexpr int kThrRows = TM / RM;
+  static_assert(kThrCols * kThrRows == kThreads, "256 threads per tile");
+  static constexpr int kGroupRowStride = TM / (RM / 4);
+  static constexpr int kGroupColStride = TN / (RN / 4);
+  static constexpr int kLdA = TM + kPad;  // sA[k][row]
+  static constexpr int kLdB = TN + kPad;  // sB[k][col]
+  static constexpr int kQuadsA = TM * kKC / 4;
+  static constexpr int kQuadsB = kKC * TN / 4;
+  static constexpr int kLoadsA = (kQuadsA + kThreads - 1) / kThreads;
+  static constexpr int kLoadsB = (kQuadsB + kThreads - 1) / kThreads;
+  static constexpr int kLdsElems = 2 * kKC * (kLdA + kLdB);
+};
+
+template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
+__device__ __forceinline__ void minplus_tile(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                             int64_t row0, int64_t col0, int64_t kb0,
+                                             T* __restrict__ lds) {
+  using S = TileShape<T, TM, TN, RM, RN>;
+  T* sA = lds;                              // [2][kKC][kLdA]
+  T* sB = lds + 2 * kKC * S::kLdA;          // [2][kKC][kLdB]
+
+  const int tid = threadIdx.x;
+  const int tc = tid % S::kThrCols;
+  const int tr = tid / S::kThrCols;
+
+  // Prefetch registers for one chunk of A and B.
+  T ga[S::kLoadsA][4];
+  T gb[S::kLoadsB][4];
+
+  auto fetch = [&](int chunk) {
+    const int64_t k0 = kb0 + (int64_t)chunk * kKC;
+#pragma unroll
+    for (int l = 0; l < S::kLoadsA; ++l) {
+      const int q = tid + l * kThreads;
+      if (S::kQuadsA % kThreads == 0 || q < S::kQuadsA) {
+        const int r = q / (kKC / 4), kq = q % (kKC / 4);
+        gload4<T, VEC, EDGE>(d, ld, n, row0 + r, k0 + kq * 4, inf, ga[l]);
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < S::kLoadsB; ++l) {
+      const int q = tid + l * kThreads;
+      if (S::kQuadsB % kThreads == 0 || q < S::kQuadsB) {
+        const int kr = q / (TN / 4), cq = q % (TN / 4);
+        gload4<T, VEC, EDGE>(d, ld, n, k0 + kr, col0 + cq * 4, inf, gb[l]);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+    T* a = sA + buf * kKC * S::kLdA;
+    T* b = sB + buf * kKC * S::kLdB;
+#pragma unroll
+    for (int l = 0; l < S::kLoadsA; ++l) {
+      const int q = tid + l * kThreads;
+      if (S::kQuadsA % kThreads == 0 || q < S::kQuadsA) {
+        const int r = q / (kKC / 4), kq = q % (kKC / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[(kq * 4 + e) * S::kLdA + r] = ga[l][e];
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < S::kLoadsB; ++l) {
+      const int q = tid + l * kThreads;
+      if (S::kQuadsB % kThreads == 0 || q < S::kQuadsB) {
+        const int kr = q / (TN / 4), cq = q % (TN / 4);
+        store4(b + kr * S::kLdB + cq * 4, gb[l]);
+      }
+    }
+  };
+
+  fetch(0);
+
+  // C tile into registers.
+  T acc[RM][RN];
+#pragma unroll
+  for (int gi = 0; gi < RM / 4; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + gi * S::kGroupRowStride + tr * 4 + i;
+#pragma unroll
+      for (int gj = 0; gj < RN / 4; ++gj) {
+        T v[4];
+        gload4<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, inf, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[gi * 4 + i][gj * 4 + j] = v[j];
+      }
+    }
+
+  stash(0);
+  __syncthreads();
+
+  constexpr int kChunks = kB / kKC;
+#pragma unroll 1
+  for (int c = 0; c < kChunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < kChunks) fetch(c + 1);
+    const T* a = sA + buf * kKC * S::kLdA;
+    const T* b = sB + buf * kKC * S::kLdB;
+#pragma unroll
+    for (int k = 0; k < kKC; k += 2) {
+      T a0[RM], b0[RN], a1[RM], b1[RN];
+#pragma unroll
+      for (int gi = 0; gi < RM / 4; ++gi) {
+        T v[4];
+        load4(a + k * S::kLdA + gi * S::kGroupRowStride + tr * 4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a0[gi * 4 + i] = v[i];
+        load4(a + (k + 1) * S::kLdA + gi * S::kGroupRowStride + tr * 4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a1[gi * 4 + i] = v[i];
+      }
+#pragma unroll
+      for (int gj = 0; gj < RN / 4; ++gj) {
+        T v[4];
+        load4(b + k * S::kLdB + gj * S::kGroupColStride + tc * 4, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b0[gj * 4 + j] = v[j];
+        load4(b + (k + 1) * S::kLdB + gj * S::kGroupColStride + tc * 4, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b1[gj * 4 + j] = v[j];
+      }
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j)
+          acc[i][j] = mp_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+    }
+    if (c + 1 < kChunks) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int gi = 0; gi < RM / 4; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + gi * S::kGroupRowStride + tr * 4 + i;
+#pragma unroll
+      for (int gj = 0; gj < RN / 4; ++gj) {
+        T v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = acc[gi * 4 + i][gj * 4 + j];
+        gstore4<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, v);
+      }
+    }
+}
+
+template <typename T, int TM, int TN, int RM, int RN, bool VEC>
+__device__ __forceinline__ void minplus_tile_dispatch(T* __restrict__ d, int64_t n, int64_t ld,
+                                                      T inf, int64_t row0, int64_t col0,
+                                                      int64_t kb0, T* __restrict__ lds) {
+  const bool interior = row0 + TM <= n && col0 + TN <= n && kb0 + kB <= n;
+  if (interior)
+    minplus_tile<T, TM, TN, RM, RN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds);
+  else
+    minplus_tile<T, TM, TN, RM, RN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds);
+}
+
+// Phase-2 panel tiles: the row panel is split into kB x kP2 tiles, the column
+// panel into kP2 x kB tiles.
+constexpr int kP2 = 32;
+using P2Row = TileShape<int32_t, kB, kP2, 4, 4>;
+using P2Col = TileShape<int32_t, kP2, kB, 4, 4>;
+using P3 = TileShape<int32_t, kB, kB, 8, 8>;
+constexpr int kLdsP2 = P2Row::kLdsElems > P2Col::kLdsElems ? P2Row::kLdsElems : P2Col::kLdsElems;
+constexpr int kLdsP3 = P3::kLdsElems;
+
+// ---------------------------------------------------------------------------
+// Phase 1: close the diagonal block D_KK (Floyd-Warshall inside the block).
+// 1024 threads as 32 x 32, each owning a 4 x 4 sub-block in registers.  Before
+// pivot t, the owners of column t and row t publish them into LDS; pivot row
+// and column do not change during their own step (d[t][t] >= 0), so one
+// barrier per pivot orders everything.
+// ---------------------------------------------------------------------------
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(1024) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
+                                                  T inf, int64_t K) {
+  __shared__ __attribute__((aligned(16))) T colv[2][kB];
+  __shared__ __attribute__((aligned(16))) T rowv[2][kB];
+  const int tx = threadIdx.x & 31;
+  const int ty = threadIdx.x >> 5;
+  const int64_t base = K * kB;
+  const bool edge = base + kB > n;
+
+  T r[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (edge) gload4<T, VEC, true>(d, ld, n, base + ty * 4 + i, base + tx * 4, inf, r[i]);
+    else gload4<T, VEC, false>(d, ld, n, base + ty * 4 + i, base + tx * 4, inf, r[i]);
+  }
+
+  if (tx == 0) {
+    T v[4] = {r[0][0], r[1][0], r[2][0], r[3][0]};
+    store4(&colv[0][ty * 4], v);
+  }
+  if (ty == 0) store4(&rowv[0][tx * 4], r[0]);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int t4 = 0; t4 < kB / 4; ++t4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int p = c & 1;  // t = 4*t4 + c, so t & 1 == c & 1
+      T a[4], b[4];
+      load4(&colv[p][ty * 4], a);
+      load4(&rowv[p][tx * 4], b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[i][j] = mp_min(r[i][j], a[i] + b[j]);
+      // publish pivot t+1 (its values after this step)
+      const int c1 = (c + 1) & 3;
+      const int owner = (c == 3) ? t4 + 1 : t4;
+      if (owner < kB / 4) {
+        if (tx == owner) {
+          T v[4] = {r[0][c1], r[1][c1], r[2][c1], r[3][c1]};
+          store4(&colv[p ^ 1][ty * 4], v);
+        }
+        if (ty == owner) store4(&rowv[p ^ 1][tx * 4], r[c1]);
+      }
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (edge) gstore4<T, VEC, true>(d, ld, n, base + ty * 4 + i, base + tx * 4, r[i]);
+    else gstore4<T, VEC, false>(d, ld, n, base + ty * 4 + i, base + tx * 4, r[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2: pivot-row tiles (blocks 0 .. nr-1) then pivot-column tiles.
+// ---------------------------------------------------------------------------
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+fw_phase2(T* __restrict__ d, int64_t n, int64_t ld,
+                                                      T inf, int64_t K, int64_t nb) {
+  __shared__ __attribute__((aligned(16))) T lds[kLdsP2];
+  constexpr int kSub = kB / kP2;
+  const int64_t nr = (nb - 1) * kSub;
+  int64_t b = blockIdx.x;
+  const int64_t kb0 = K * kB;
+  if (b < nr) {
+    const int64_t jp = b / kSub, sub = b % kSub;
+    const int64_t J = jp + (jp >= K);
+    const int64_t col0 = J * kB + sub * kP2;
+    if (col0 >= n) return;
+    minplus_tile_dispatch<T, kB, kP2, 4, 4, VEC>(d, n, ld, inf, kb0, col0, kb0, lds);
+  } else {
+    b -= nr;
+    const int64_t ip = b / kSub, sub = b % kSub;
+    const int64_t I = ip + (ip >= K);
+    const int64_t row0 = I * kB + sub * kP2;
+    if (row0 >= n) return;
+    minplus_tile_dispatch<T, kP2, kB, 4, 4, VEC>(d, n, ld, inf, row0, kb0, kb0, lds);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 3: every tile (I, J) with I != K and J != K.
+// ---------------------------------------------------------------------------
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
+fw_phase3(T* __restrict__ d, int64_t n, int64_t ld,
+                                                      T inf, int64_t K, int64_t nb) {
+  __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
+  const int64_t m = nb - 1;
+  const int64_t b = blockIdx.x;
+  const int64_t ip = b / m, jp = b % m;
+  const int64_t I = ip + (ip >= K), J = jp + (jp >= K);
+  minplus_tile_dispatch<T, kB, kB, 8, 8, VEC>(d, n, ld, inf, I * kB, J * kB, K * kB, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+thread_local int g_last_hip_error = 0;
+
+// Per-device cache: 0 = unknown, 1 = gfx950, 2 = other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return APSP_ERR_NO_DEVICE;
+  if (dev < kMaxDevices) {
+    int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return APSP_OK;
+    if (s == 2) return APSP_ERR_NO_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return APSP_ERR_NO_DEVICE;
+  const char* a = prop.gcnArchName;
+  const bool ok = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+                  a[5] == '0' && (a[6] == '\0' || a[6] == ':');
+  if (dev < kMaxDevices) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? APSP_OK : APSP_ERR_NO_DEVICE;
+}
+
+template <typename T>
+bool inf_ok(T inf);
+template <>
+bool inf_ok<int32_t>(int32_t inf) { return inf >= 1 && inf <= 0x3FFFFFFF; }
+template <>
+bool inf_ok<float>(float inf) { return inf > 0.0f; }  // false for NaN
+
+template <typename T>
+int validate(const T* d, int64_t n, int64_t ld, T inf) {
+  if (n < 0) return APSP_ERR_INVALID_VALUE;
+  if (n == 0) return APSP_OK;
+  if (d == nullptr) return APSP_ERR_INVALID_VALUE;
+  if (ld < n) return APSP_ERR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(d) % sizeof(T)) != 0) return APSP_ERR_INVALID_VALUE;
+  if (n > (int64_t(1) << 31)) return APSP_ERR_INVALID_VALUE;
+  if (ld > INT64_MAX / (int64_t)sizeof(T) / n) return APSP_ERR_INVALID_VALUE;
+  if (!inf_ok<T>(inf)) return APSP_ERR_INVALID_VALUE;
+  return APSP_OK;
+}
+
+struct PhaseTimer {
+  // Events bracketing each launch: ev[2*i] before, ev[2*i+1] after launch i.
+  hipEvent_t* ev = nullptr;
+  int* phase = nullptr;
+  int64_t cap = 0, used = 0;
+};
+
+template <typename T, bool VEC>
+int enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
+                   PhaseTimer* tm) {
+  const int64_t nb = (n + kB - 1) / kB;
+  auto mark = [&](int phase, bool before) {
+    if (!tm) return;
+    if (before) {
+      (void)hipEventRecord(tm->ev[2 * tm->used], s);
+      tm->phase[tm->used] = phase;
+    } else {
+      (void)hipEventRecord(tm->ev[2 * tm->used + 1], s);
+      ++tm->used;
+    }
+  };
+  for (int64_t K = r0; K < r1; ++K) {
+    mark(0, true);
+    hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(1024), 0, s, d, n, ld, inf, K);
+    mark(0, false);
+    if (nb > 1) {
+      const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
+      mark(1, true);
+      hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n,
+                         ld, inf, K, nb);
+      mark(1, false);
+      const int64_t g3 = (nb - 1) * (nb - 1);
+      mark(2, true);
+      hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n,
+                         ld, inf, K, nb);
+      mark(2, false);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return APSP_ERR_LAUNCH;
+  }
+  return APSP_OK;
+}
+
+template <typename T>
+int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream,
+        PhaseTimer* tm) {
+  int st = validate<T>(d, n, ld, inf);
+  if (st != APSP_OK) return st;
+  const int64_t nb = n == 0 ? 0 : (n + kB - 1) / kB;
+  if (r0 < 0 || r1 < r0 || r1 > nb) return APSP_ERR_INVALID_VALUE;
+  if (n == 0 || r0 == r1) return APSP_OK;
+  st = check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+  return vec ? enqueue_rounds<T, true>(d, n, ld, inf, r0, r1, s, tm)
+             : enqueue_rounds<T, false>(d, n, ld, inf, r0, r1, s, tm);
+}
+
+template <typename T>
+int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms,
+              int64_t* phase_launch) {
+  int st = validate<T>(d, n, ld, inf);
+  if (st != APSP_OK) return st;
+  if (phase_ms) for (int p = 0; p < 3; ++p) phase_ms[p] = 0.0;
+  if (phase_launch) for (int p = 0; p < 3; ++p) phase_launch[p] = 0;
+  if (n == 0) return APSP_OK;
+  st = check_device();
+  if (st != APSP_OK) return st;
+  const int64_t nb = (n + kB - 1) / kB;
+  PhaseTimer tm;
+  tm.cap = 3 * nb;
+  tm.ev = new hipEvent_t[2 * tm.cap];
+  tm.phase = new int[tm.cap];
+  int64_t created = 0;
+  for (; created < 2 * tm.cap; ++created)
+    if (hipEventCreate(&tm.ev[created]) != hipSuccess) break;
+  if (created < 2 * tm.cap) {
+    for (int64_t i = 0; i < created; ++i) (void)hipEventDestroy(tm.ev[i]);
+    delete[] tm.ev;
+    delete[] tm.phase;
+    g_last_hip_error = (int)hipGetLastError();
+    return APSP_ERR_LAUNCH;
+  }
+  st = run<T>(d, n, ld, inf, 0, nb, stream, &tm);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess && st == APSP_OK) {
+    g_last_hip_error = (int)hipGetLastError();
+    st = APSP_ERR_LAUNCH;
+  }
+  if (st == APSP_OK) {
+    for (int64_t i = 0; i < tm.used; ++i) {
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, tm.ev[2 * i], tm.ev[2 * i + 1]);
+      const int p = tm.phase[i];
+      if (phase_ms) phase_ms[p] += ms;
+      if (phase_launch) phase_launch[p] += 1;
+    }
+  }
+  for (int64_t i = 0; i < 2 * tm.cap; ++i) (void)hipEventDestroy(tm.ev[i]);
+  delete[] tm.ev;
+  delete[] tm.phase;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int apsp_fw_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream) {
+  const int64_t nb = n > 0 ? (n + kB - 1) / kB : 0;
+  return run<int32_t>(d, n, ld, inf, 0, nb, stream, nullptr);
+}
+
+int apsp_fw_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
+  const int64_t nb = n > 0 ? (n + kB - 1) / kB : 0;
+  return run<float>(d, n, ld, inf, 0, nb, stream, nullptr);
+}
+
+int apsp_fw_rounds_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t round_begin,
+                       int64_t round_end, void* stream) {
+  return run<int32_t>(d, n, ld, inf, round_begin, round_end, stream, nullptr);
+}
+
+int apsp_fw_rounds_f32(float* d, int64_t n, int64_t ld, float inf, int64_t round_begin,
+                       int64_t round_end, void* stream) {
+  return run<float>(d, n, ld, inf, round_begin, round_end, stream, nullptr);
+}
+
+int apsp_fw_timed_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream,
+                      double* phase_ms, int64_t* phase_launch) {
+  return run_timed<int32_t>(d, n, ld, inf, stream, phase_ms, phase_launch);
+}
+
+int apsp_fw_timed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream,
+                      double* phase_ms, int64_t* phase_launch) {
+  return run_timed<float>(d, n, ld, inf, stream, phase_ms, phase_launch);
+}
+
+int64_t apsp_pivot_block(int64_t n) {
+  (void)n;
+  return kB;
+}
+
+const char* apsp_status_string(int status) {
+  switch (status) {
+    case APSP_OK: return "APSP_OK";
+    case APSP_ERR_INVALID_VALUE: return "APSP_ERR_INVALID_VALUE: invalid argument";
+    case APSP_ERR_NO_DEVICE: return "APSP_ERR_NO_DEVICE: current device is not gfx950";
+    case APSP_ERR_LAUNCH: return "APSP_ERR_LAUNCH: kernel launch failed";
+    default: return "APSP: unknown status";
+  }
+}
+
+int apsp_last_hip_error(void) { return g_last_hip_error; }
+
+int apsp_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+/*
+ * apsp.h -- C ABI of the gfx950 (MI355X) blocked Floyd-Warshall library.
+ *
+ * The library computes all-pairs shortest-path distances of a weighted
+ * digraph held as a dense row-major distance matrix in device memory, by the
+ * blocked Floyd-Warshall method of the page "Katz and Kider" (thesis section
+ * 4.6 and its Algorithms 16-18): the matrix is cut into square pivot blocks;
+ * round K closes the diagonal block (K,K) (Phase 1), then updates the blocks
+ * in pivot row K and pivot column K (Phase 2), then every remaining block
+ * (Phase 3), and the pivot moves one block down the diagonal.
+ *
+ * Only plain C types cross this boundary.  `stream` is a hipStream_t passed
+ * as an opaque pointer (NULL = the null stream).
+ *
+ * Matrix contract (all entry points):
+ *   d      device pointer to element (0,0); element (i,j) is d[i*ld + j].
+ *          Must be 4-byte aligned.  When d is 16-byte aligned and ld is a
+ *          multiple of 4, 128-bit loads and stores are used.
+ *   n      number of vertices, n >= 0 (n = 0 is a no-op).
+ *   ld     leading dimension in elements, ld >= max(n, 1).
+ *   inf    the "no edge / no path" sentinel.
+ * Input preconditions (not checked; results are undefined otherwise):
+ *   d[i][i] = 0; 0 <= d[i][j] <= inf; no NaN; every true shortest distance
+ *   between connected vertices is < inf.
+ * Output: on completion of the enqueued work, d[i][j] (i, j < n) holds the
+ * shortest-path distance from i to j, and exactly `inf` when j is not
+ * reachable from i.  Elements outside the leading n x n block are never read
+ * or written.  int32 results are exact; float32 results are within a few
+ * units in the last place per path edge of the exact real-number distances,
+ * and bit-identical from run to run.
+ *
+ * Ownership and concurrency: the caller owns d.  The library allocates no
+ * device memory and keeps no state beyond a per-device "is gfx950" cache, so
+ * calls on different streams with different matrices may run concurrently.
+ * Work is enqueued asynchronously on `stream`; the caller synchronises.
+ *
+ * Errors: argument errors return APSP_ERR_INVALID_VALUE before any HIP call
+ * (nothing is enqueued, d is untouched).  A current device that is not
+ * gfx950 returns APSP_ERR_NO_DEVICE.  A failed launch returns APSP_ERR_LAUNCH
+ * (d is then undefined) and apsp_last_hip_error() gives the hipError_t value
+ * for the calling thread.  Nothing is printed; nothing aborts.
+ */
+#ifndef APSP_H
+#define APSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  APSP_OK = 0,
+  APSP_ERR_INVALID_VALUE = 1,
+  APSP_ERR_NO_DEVICE = 2,
+  APSP_ERR_LAUNCH = 3
+};
+
+/*
+ * All-pairs shortest paths on an int32 matrix, in place (all rounds).
+ * Arithmetic: plain int32 add and signed min.  inf must satisfy
+ * 1 <= inf <= 0x3FFFFFFF so that inf + inf cannot overflow.
+ * Defines: "Katz and Kider" page, section 4.6 (three phases per round).
+ */
+int apsp_fw_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream);
+
+/*
+ * All-pairs shortest paths on a float32 matrix, in place (all rounds).
+ * Arithmetic: IEEE binary32 add (round to nearest even) and min.
+ * inf must be > 0 and not NaN; +infinity is allowed.
+ * Defines: "Katz and Kider" page, section 4.6 (three phases per round).
+ */
+int apsp_fw_f32(float *d, int64_t n, int64_t ld, float inf, void *stream);
+
+/*
+ * Rounds [round_begin, round_end) only, in place, with pivot blocks of
+ * apsp_pivot_block(n) vertices; round r uses pivots [r*B, min((r+1)*B, n)).
+ * After rounds [0, r) the matrix holds the shortest distances over paths
+ * whose intermediate vertices all lie in [0, r*B) -- the state of the
+ * Floyd-Warshall recurrence after its first r*B pivots -- so a run can stop
+ * and later resume from that state.  Calling [0, R) and then [R, rounds)
+ * equals one full call.  Requires 0 <= round_begin <= round_end <=
+ * ceil(n / B).  Defines: "Katz and Kider" page, section 4.6 (the primary
+ * block moves one block down the diagonal per round).
+ */
+int apsp_fw_rounds_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf,
+                       int64_t round_begin, int64_t round_end, void *stream);
+int apsp_fw_rounds_f32(float *d, int64_t n, int64_t ld, float inf,
+                       int64_t round_begin, int64_t round_end, void *stream);
+
+/*
+ * Measurement variant of apsp_fw_i32 / apsp_fw_f32: the same kernels on
+ * the same stream, with HIP events recorded around each phase's launch.
+ * It synchronises the stream before returning and writes:
+ *   phase_ms[p]     summed event time of phase p+1 (p = 0, 1, 2), in ms;
+ *   phase_launch[p] number of launches of phase p+1.
+ * Either pointer may be NULL.  Errors as for apsp_fw_i32.
+ */
+int apsp_fw_timed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream,
+                      double *phase_ms, int64_t *phase_launch);
+int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
+                      double *phase_ms, int64_t *phase_launch);
+
+/* Pivot block edge B used for an n-vertex matrix (rounds = ceil(n / B)). */
+int64_t apsp_pivot_block(int64_t n);
+
+/* Static text for a status code (never NULL). */
+const char *apsp_status_string(int status);
+
+/* hipError_t of the calling thread's last APSP_ERR_LAUNCH (0 if none). */
+int apsp_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int apsp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* APSP_H */

@@ -1,0 +1,106 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import graph_all_pairs_amd as ga
+from graph_all_pairs_amd import _build
+
+HEADER = os.path.join(_build.ROOT, "include", "apsp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_build.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ga.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(apsp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(ga.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(_build.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_library_is_built_for_gfx950_only():
+    # the offload bundle carries a gfx950 code object and no other target
+    data = open(_build.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
+        assert other + b"\x00" not in data and b"amdgcn-amd-amdhsa--" + other not in data
+
+
+def test_status_strings_and_version(lib):
+    assert ga.apsp_status_string(0) == "APSP_OK"
+    for s in (1, 2, 3):
+        assert ga.apsp_status_string(s).startswith("APSP_ERR")
+    assert "unknown" in ga.apsp_status_string(99)
+    assert ga.apsp_version() >= 100
+    assert ga.apsp_pivot_block(1000) == 128
+
+
+FAKE = 0x10000  # never dereferenced: every case below is rejected first
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, -1, 4, 100),            # n < 0
+    (0, 4, 4, 100),                # null pointer with n > 0
+    (FAKE, 8, 7, 100),             # ld < n
+    (FAKE + 2, 4, 4, 100),         # not 4-byte aligned
+    (FAKE, 4, 4, 0),               # inf < 1
+    (FAKE, 4, 4, 0x40000000),      # inf + inf would overflow int32
+    (FAKE, 4, 4, -5),
+    (FAKE, (1 << 31) + 1, (1 << 31) + 1, 100),  # too large
+])
+def test_i32_argument_errors(lib, args):
+    assert ga.apsp_fw_i32(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("inf", [0.0, -1.0, float("nan"), -float("inf")])
+def test_f32_bad_inf(lib, inf):
+    assert ga.apsp_fw_f32(FAKE, 4, 4, inf, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_round_range_errors(lib):
+    # 300 vertices -> 3 rounds of 128
+    assert ga.apsp_fw_rounds_i32(FAKE, 300, 300, 100, -1, 1) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_fw_rounds_i32(FAKE, 300, 300, 100, 2, 1) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_fw_rounds_i32(FAKE, 300, 300, 100, 0, 4) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_fw_rounds_f32(FAKE, 300, 300, 1.0, 0, 4) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_empty_is_a_no_op(lib):
+    assert ga.apsp_fw_i32(0, 0, 1, 100, 0) == ga.APSP_OK
+    assert ga.apsp_fw_f32(0, 0, 1, 1.0, 0) == ga.APSP_OK
+    assert ga.apsp_fw_rounds_i32(FAKE, 300, 300, 100, 1, 1) == ga.APSP_OK
+
+
+def test_timed_variant_validates_too(lib):
+    st, ms, cnt = ga.apsp_fw_timed_i32(0, 4, 4, 100)
+    assert st == ga.APSP_ERR_INVALID_VALUE and cnt == [0, 0, 0] or st == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        ga.load(str(tmp_path / "nope.so"))
+
+
+def test_single_hip_runtime_in_process(lib):
+    # torch and libapsp.so must share one libamdhip64 (see graph_all_pairs_amd.load)
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(paths) == 1, paths

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+int32 results must be bit-exact; float32 results must be within 1e-5
+relative of the oracle's binary64 distances (exact where the distance is 0
+or unreachable) and bit-identical from run to run.
+"""
+import numpy as np
+import torch  # noqa: F401  (imported at collection, before any test timer starts)
+import pytest
+
+import graph_all_pairs_amd as ga
+import graphgen as gg
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+INF = gg.INF_I32
+F32_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, torch.device("cuda:0")
+
+
+def gpu_apsp(torch_dev, w, inf, ld=None, offset=0):
+    """Copy w (n x ld_w) to the device, run the C-ABI entry point, return the
+    full device buffer (n x ld) as numpy."""
+    torch, dev = torch_dev
+    n = w.shape[0]
+    ld = w.shape[1] if ld is None else ld
+    assert ld >= w.shape[1]
+    host = np.zeros((n, ld + offset), dtype=w.dtype)
+    canary = np.array(-7, dtype=w.dtype)
+    host[:, :] = canary
+    host[:, offset:offset + w.shape[1]] = w
+    buf = torch.from_numpy(host.reshape(-1)).to(dev)
+    ptr = buf.data_ptr() + offset * w.dtype.itemsize
+    s = torch.cuda.current_stream().cuda_stream
+    fn = ga.apsp_fw_i32 if w.dtype == np.int32 else ga.apsp_fw_f32
+    st = fn(ptr, n, ld + offset if offset else ld, inf, s)
+    assert st == ga.APSP_OK, ga.apsp_status_string(st)
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy().reshape(n, ld + offset)
+    return out[:, offset:] if offset else out
+
+
+def assert_f32_close(got, want):
+    got = got.astype(np.float64)
+    assert np.array_equal(np.isinf(got), np.isinf(want))
+    fin = np.isfinite(want)
+    g, o = got[fin], want[fin]
+    assert np.all((o == 0) == (g == 0))
+    rel = np.abs(g - o) / np.maximum(np.abs(o), np.finfo(np.float64).tiny)
+    assert float(rel.max(initial=0.0)) <= F32_RTOL, float(rel.max())
+
+
+SIZES = [1, 2, 3, 5, 31, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 997, 1000, 1024, 1031]
+
+
+def family(name, n, seed):
+    if name == "er":
+        p = min(1.0, 4.0 / max(n, 1))      # sparse: some pairs stay unreachable
+        return gg.erdos_renyi(n, p, 1, 100, seed)
+    if name == "er_dense":
+        return gg.erdos_renyi(n, 0.3, 1, 1000, seed)
+    if name == "complete":
+        return gg.complete(n, 1, 10000, seed)
+    if name == "ring":
+        return gg.ring(n, 3)
+    if name == "two_rings":
+        return gg.two_rings(n // 2, n - n // 2, 2)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("fam", ["er", "complete", "ring", "two_rings"])
+def test_int32_sweep(torch_dev, n, fam):
+    print(f"case int32 {fam} n={n}", flush=True)
+    w = family(fam, n, 100 + n)
+    got = gpu_apsp(torch_dev, w, INF)
+    assert np.array_equal(got, oracle.fw_i32(w))
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("fam", ["er_dense", "complete_f32", "ring_half"])
+def test_float32_sweep(torch_dev, n, fam):
+    print(f"case float32 {fam} n={n}", flush=True)
+    if fam == "complete_f32":
+        w = gg.complete_f32(n, 200 + n)
+    elif fam == "ring_half":
+        w = gg.ring(n, 0.5, dtype=np.float32, inf=np.inf)
+    else:
+        wi = gg.erdos_renyi(n, min(1.0, 6.0 / max(n, 1)), 1, 1000, 300 + n)
+        w = np.where(wi == INF, np.inf, wi.astype(np.float64) * 0.013).astype(np.float32)
+    got = gpu_apsp(torch_dev, w, np.inf)
+    want = oracle.fw_f64(w.astype(np.float64))
+    assert_f32_close(got, want)
+    if fam == "ring_half":   # exact in binary32: whole multiples of 0.5
+        assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_hand_example(torch_dev):
+    from _helpers import read_golden
+    g = read_golden("hand4_fw.txt", INF)
+    got = gpu_apsp(torch_dev, g["input"].astype(np.int32), INF)
+    assert np.array_equal(got, g["final"])
+
+
+@pytest.mark.parametrize("n,ld", [(45, 64), (300, 313), (257, 260), (1000, 1024), (129, 131)])
+def test_leading_dimension_and_canary(torch_dev, n, ld):
+    print(f"case ld n={n} ld={ld}", flush=True)
+    w = gg.erdos_renyi(n, 0.05, 1, 50, n, ld=ld, canary=-7)
+    got = gpu_apsp(torch_dev, w, INF)
+    assert np.all(got[:, n:] == -7), "padding columns were written"
+    assert np.array_equal(got[:, :n], oracle.fw_i32(w)[:, :n])
+
+
+@pytest.mark.parametrize("n", [130, 300])
+def test_unaligned_pointer_uses_scalar_path(torch_dev, n):
+    # pointer 4 bytes past a 16-byte boundary, ld not a multiple of 4
+    w = gg.erdos_renyi(n, 0.05, 1, 50, 7 + n)
+    got = gpu_apsp(torch_dev, w, INF, offset=1)
+    assert np.array_equal(got[:, :n], oracle.fw_i32(w))
+
+
+def test_inf_preserved_between_components(torch_dev):
+    w = gg.two_rings(200, 171, 5)
+    got = gpu_apsp(torch_dev, w, INF)
+    assert np.all(got[:200, 200:] == INF) and np.all(got[200:, :200] == INF)
+    wf = gg.two_rings(200, 171, 0.25, dtype=np.float32, inf=np.inf)
+    gotf = gpu_apsp(torch_dev, wf, np.inf)
+    assert np.all(np.isinf(gotf[:200, 200:]))
+    # a finite float sentinel behaves the same way
+    wf2 = np.where(np.isinf(wf), np.float32(1e30), wf)
+    gotf2 = gpu_apsp(torch_dev, wf2, 1e30)
+    assert np.all(gotf2[:200, 200:] == np.float32(1e30))
+
+
+def test_rounds_resume_matches_partial_oracle(torch_dev):
+    torch, dev = torch_dev
+    n = 300
+    B = ga.apsp_pivot_block(n)
+    w = gg.erdos_renyi(n, 0.02, 1, 100, 17)
+    t = torch.from_numpy(w).to(dev)
+    rounds = (n + B - 1) // B
+    for r in range(rounds):
+        ga.fw_rounds(t, r, r + 1, INF)
+        torch.cuda.synchronize()
+        want = oracle.fw_i32(w, k_end=min((r + 1) * B, n))
+        assert np.array_equal(t.cpu().numpy(), want), f"after round {r}"
+
+
+def test_repeat_runs_bit_identical_float(torch_dev):
+    w = gg.complete_f32(1031, 99)
+    a = gpu_apsp(torch_dev, w, np.inf)
+    b = gpu_apsp(torch_dev, w, np.inf)
+    assert np.array_equal(a.view(np.int32), b.view(np.int32))
+
+
+def test_two_streams_two_matrices(torch_dev):
+    torch, dev = torch_dev
+    w1 = gg.erdos_renyi(700, 0.01, 1, 100, 1)
+    w2 = gg.complete(650, 1, 100, 2)
+    t1 = torch.from_numpy(w1).to(dev)
+    t2 = torch.from_numpy(w2).to(dev)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        ga.fw(t1, INF)
+    with torch.cuda.stream(s2):
+        ga.fw(t2, INF)
+    torch.cuda.synchronize()
+    assert np.array_equal(t1.cpu().numpy(), oracle.fw_i32(w1))
+    assert np.array_equal(t2.cpu().numpy(), oracle.fw_i32(w2))
+
+
+def test_timed_variant_counts_launches(torch_dev):
+    torch, dev = torch_dev
+    n = 1000
+    w = gg.erdos_renyi(n, 0.01, 1, 100, 5)
+    t = torch.from_numpy(w).to(dev)
+    ms, cnt = ga.fw_timed(t, INF)
+    nb = (n + 127) // 128
+    assert cnt == [nb, nb, nb]
+    assert all(x > 0 for x in ms)
+    assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+
+
+def test_tensor_wrapper_errors(torch_dev):
+    torch, dev = torch_dev
+    with pytest.raises(ValueError):
+        ga.fw(torch.zeros((4, 4), dtype=torch.float64, device=dev))
+    with pytest.raises(ValueError):
+        ga.fw(torch.zeros((4, 3), dtype=torch.int32, device=dev))
+    with pytest.raises(ga.APSPError):
+        ga.fw(torch.zeros((4, 4), dtype=torch.int32, device=dev), inf=0)
