@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput bench: blocked Floyd-Warshall APSP on one MI355X.
+
+One step = one full all-pairs shortest-path call (every round: Phase 1,
+Phase 2, Phase 3) over its own fresh copy of the seeded synthetic matrix,
+which is resident in HBM before the timed region starts.
+
+Prints ONE JSON line:
+  value        relaxations/s = n^3 / (wall time per step), n = logical size
+  roofline     the Phase-3 kernel (the hot loop): algorithmic relaxations per
+               launch / its average launch duration (HIP events recorded on
+               the kernel's stream around every launch, inside the timed
+               region), against the int32 VALU min-plus peak
+  cpu_baseline the CPU oracle (plain Floyd-Warshall) timed on this host on a
+               bounded sample of the same workload: its first k pivots
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "APSP min-plus relaxations/s (n^3/time) at n=8192; % of VALU roofline"
+DEFAULT_WORKLOAD = "complete-8192-i32"
+
+# MI355X VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 32-bit lane
+# instructions/s.  A relaxation (one add, one min) costs 1.5 instructions when
+# two candidates share one three-input min: v_add + v_add + v_min3 per pair.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+INSTR_PER_RELAX = 1.5
+PEAK_RELAX = VALU_LANE_OPS / INSTR_PER_RELAX        # 2.62e13 relaxations/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def phase3_relaxations_per_round(n: int, B: int) -> list[int]:
+    """Algorithmic (logical-n) relaxations done by Phase 3 in each round:
+    rows and columns outside pivot block K, times the pivots in block K."""
+    out = []
+    nb = (n + B - 1) // B
+    for K in range(nb):
+        bk = min(B, n - K * B)
+        out.append((n - bk) * (n - bk) * bk)
+    return out
+
+
+def source_sha() -> str:
+    p = os.path.join(ROOT, "graph_all_pairs_amd", "csrc", "apsp.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def read_traffic(workload: str, per_launch_relax: float):
+    """HBM bytes per Phase-3 launch from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"phase3_hbm_traffic_{workload}.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the oracle's plain Floyd-Warshall on the first k pivots."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    n = w.shape[0]
+    f64 = w.dtype != np.int32
+
+    def run(k):
+        a = w.astype(np.float64) if f64 else np.array(w, copy=True)
+        t0 = time.perf_counter()
+        (orc.lib.oracle_fw_f64 if f64 else orc.lib.oracle_fw_i32)(a.ctypes.data, n, a.shape[1], k)
+        return time.perf_counter() - t0
+
+    probe = min(n, 4)
+    per_pivot = run(probe) / probe
+    k = int(max(1, min(n, target_s / max(per_pivot, 1e-9))))
+    dt = run(k)
+    return {
+        "value": k * n * n / dt,
+        "unit": "relaxations/s",
+        "cores": orc.threads(),
+        "kind": "oracle",
+        "sample": f"plain Floyd-Warshall (k outermost, OpenMP over rows) on the same "
+                  f"{n}x{n} matrix, first {k} of {n} pivots ({k * n * n:.3e} relaxations) "
+                  f"in {dt:.2f} s; rate = relaxations / time",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--ld", type=int, default=None, help="leading dimension (default n)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import graph_all_pairs_amd as ga
+    import graphgen as gg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spec = gg.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    w = gg.make_workload(args.workload, ld=args.ld)
+    n, ld = w.shape[0], w.shape[1]
+    sha = gg.sha256_matrix(w, n)
+    log(f"workload {args.workload}: n={n} ld={ld} built in {time.perf_counter() - t0:.1f} s "
+        f"sha256={sha[:16]}")
+    is_int = w.dtype == np.int32
+    inf = gg.INF_I32 if is_int else float("inf")
+    B = ga.apsp_pivot_block(n)
+    nb = (n + B - 1) // B
+
+    pristine = torch.from_numpy(w).to(dev)
+    copies = [torch.empty_like(pristine) for _ in range(args.warmup + args.steps)]
+    for c in copies:
+        c.copy_(pristine)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    fn = ga.apsp_fw_timed_i32 if is_int else ga.apsp_fw_timed_f32
+
+    def step(t):
+        st, ms, cnt = fn(t.data_ptr(), n, ld, inf, sptr)
+        if st != ga.APSP_OK:
+            raise ga.APSPError(st, "apsp_fw_timed")
+        return ms, cnt
+
+    for i in range(args.warmup):
+        step(copies[i])
+    log(f"warmup {args.warmup} done")
+
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    phase_ms = [0.0, 0.0, 0.0]
+    launches = [0, 0, 0]
+    ev0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        ms, cnt = step(copies[args.warmup + i])
+        for p in range(3):
+            phase_ms[p] += ms[p]
+            launches[p] += cnt[p]
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+    value = float(n) ** 3 / (wall / args.steps)
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms, events {ev_ms:.1f} ms, "
+        f"phases ms/step {[round(x / args.steps, 3) for x in phase_ms]}")
+
+    # Phase-3 roofline: algorithmic relaxations per launch / mean launch time.
+    p3_relax = sum(phase3_relaxations_per_round(n, B)) * args.steps
+    p3_launch = launches[2]
+    p3_ms_avg = phase_ms[2] / max(p3_launch, 1)
+    relax_per_launch = p3_relax / max(p3_launch, 1)
+    achieved = relax_per_launch / (p3_ms_avg * 1e-3) if p3_ms_avg > 0 else 0.0
+    traffic = read_traffic(args.workload, relax_per_launch)
+    roofline = {
+        "bound": "alu",
+        "kernel": "fw_phase3",
+        "achieved": achieved / 1e12,
+        "peak": PEAK_RELAX / 1e12,
+        "unit": "Trelax/s",
+        "frac": achieved / PEAK_RELAX,
+        "traffic": traffic,
+        "relax_per_launch": relax_per_launch,
+        "avg_launch_ms": p3_ms_avg,
+        "launches": p3_launch,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.3e} relax/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "relaxations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "int32" if is_int else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "n": n, "ld": ld, "seed": spec["seed"], "pivot_block": B, "rounds": nb,
+            "input_sha256": sha,
+        },
+        "phase_ms_per_step": [x / args.steps for x in phase_ms],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

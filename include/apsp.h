@@ -92,8 +92,10 @@ int apsp_fw_rounds_f32(float *d, int64_t n, int64_t ld, float inf,
  * Measurement variant of apsp_fw_i32 / apsp_fw_f32: the same kernels on
  * the same stream, with HIP events recorded around each phase's launch.
  * It synchronises the stream before returning and writes:
- *   phase_ms[p]     summed event time of phase p+1 (p = 0, 1, 2), in ms;
- *   phase_launch[p] number of launches of phase p+1.
+ *   phase_ms[p]     summed event time of the launches of kind p, in ms;
+ *   phase_launch[p] number of launches of kind p;
+ * kinds: 0 = standalone Phase 1 (first round only), 1 = Phase 2,
+ * 2 = Phase 3 (which also carries the next round's Phase 1).
  * Either pointer may be NULL.  Errors as for apsp_fw_i32.
  */
 int apsp_fw_timed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream,

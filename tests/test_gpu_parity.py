@@ -185,7 +185,7 @@ def test_timed_variant_counts_launches(torch_dev):
     t = torch.from_numpy(w).to(dev)
     ms, cnt = ga.fw_timed(t, INF)
     nb = (n + 127) // 128
-    assert cnt == [nb, nb, nb]
+    assert cnt == [1, nb, nb]   # later Phase 1s run inside Phase-3 launches
     assert all(x > 0 for x in ms)
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
 
