@@ -32,12 +32,17 @@ sys.path.insert(0, ROOT)
 METRIC = "APSP min-plus relaxations/s (n^3/time) at n=8192; % of VALU roofline"
 DEFAULT_WORKLOAD = "complete-8192-i32"
 
-# MI355X VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 32-bit lane
-# instructions/s.  A relaxation (one add, one min) costs 1.5 instructions when
-# two candidates share one three-input min: v_add + v_add + v_min3 per pair.
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# MI355X VALU peaks (256 CUs, 2.4 GHz).  A relaxation (one add, one min)
+# costs 1.5 VALU instructions when two candidates share one three-input min
+# (v_add, v_add, v_min3 per pair).
+#  - binary32 adds/mins issue at 128 lanes per clock per CU (the rate behind
+#    the published 157.3 TFLOP/s fp32 vector figure, FMA = 2 flops):
+#    7.86e13 lane-instructions/s -> 5.24e13 relaxations/s;
+#  - int32 adds/mins issue at 64 lanes per clock per CU:
+#    3.93e13 lane-instructions/s -> 2.62e13 relaxations/s.
 INSTR_PER_RELAX = 1.5
-PEAK_RELAX = VALU_LANE_OPS / INSTR_PER_RELAX        # 2.62e13 relaxations/s
+VALU_LANE_OPS = {"f32": 256 * 128 * 2.4e9, "int32": 256 * 64 * 2.4e9}
+PEAK_RELAX = {k: v / INSTR_PER_RELAX for k, v in VALU_LANE_OPS.items()}
 
 
 def log(msg: str) -> None:
@@ -153,10 +158,10 @@ def main() -> int:
     fn = ga.apsp_fw_timed_i32 if is_int else ga.apsp_fw_timed_f32
 
     def step(t):
-        st, ms, cnt = fn(t.data_ptr(), n, ld, inf, sptr)
+        st, ms, cnt, arith = fn(t.data_ptr(), n, ld, inf, sptr)
         if st != ga.APSP_OK:
             raise ga.APSPError(st, "apsp_fw_timed")
-        return ms, cnt
+        return ms, cnt, arith
 
     for i in range(args.warmup):
         step(copies[i])
@@ -164,13 +169,15 @@ def main() -> int:
 
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    phase_ms = [0.0, 0.0, 0.0]
-    launches = [0, 0, 0]
+    phase_ms = [0.0] * 4
+    launches = [0] * 4
+    ariths = set()
     ev0.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        ms, cnt = step(copies[args.warmup + i])
-        for p in range(3):
+        ms, cnt, arith = step(copies[args.warmup + i])
+        ariths.add(arith)
+        for p in range(4):
             phase_ms[p] += ms[p]
             launches[p] += cnt[p]
     ev1.record(stream)
@@ -179,8 +186,10 @@ def main() -> int:
     ev_ms = ev0.elapsed_time(ev1)
     ms_per_step = 1e3 * wall / args.steps
     value = float(n) ** 3 / (wall / args.steps)
+    arith = "f32" if ariths == {1} else "int32" if ariths == {0} else "mixed"
     log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms, events {ev_ms:.1f} ms, "
-        f"phases ms/step {[round(x / args.steps, 3) for x in phase_ms]}")
+        f"ms/step by kind [phase1, phase2, phase3, scan+convert] "
+        f"{[round(x / args.steps, 3) for x in phase_ms]}, arithmetic {arith}")
 
     # Phase-3 roofline: algorithmic relaxations per launch / mean launch time.
     p3_relax = sum(phase3_relaxations_per_round(n, B)) * args.steps
@@ -189,13 +198,14 @@ def main() -> int:
     relax_per_launch = p3_relax / max(p3_launch, 1)
     achieved = relax_per_launch / (p3_ms_avg * 1e-3) if p3_ms_avg > 0 else 0.0
     traffic = read_traffic(args.workload, relax_per_launch)
+    peak = PEAK_RELAX["int32" if arith == "int32" else "f32"]
     roofline = {
         "bound": "alu",
         "kernel": "fw_phase3",
         "achieved": achieved / 1e12,
-        "peak": PEAK_RELAX / 1e12,
+        "peak": peak / 1e12,
         "unit": "Trelax/s",
-        "frac": achieved / PEAK_RELAX,
+        "frac": achieved / peak,
         "traffic": traffic,
         "relax_per_launch": relax_per_launch,
         "avg_launch_ms": p3_ms_avg,
@@ -219,14 +229,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "int32" if is_int else "f32",
+        "dtype": arith,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
             "n": n, "ld": ld, "seed": spec["seed"], "pivot_block": B, "rounds": nb,
+            "matrix_dtype": "int32" if is_int else "f32",
             "input_sha256": sha,
         },
-        "phase_ms_per_step": [x / args.steps for x in phase_ms],
+        "ms_per_step_by_kind": dict(zip(["phase1", "phase2", "phase3", "scan_convert"],
+                                        [x / args.steps for x in phase_ms])),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

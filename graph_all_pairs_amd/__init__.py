@@ -11,14 +11,15 @@ streams are integers):
     apsp_fw_f32(d_ptr, n, ld, inf, stream) -> status
     apsp_fw_rounds_i32(d_ptr, n, ld, inf, r0, r1, stream) -> status
     apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream) -> status
-    apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, phase_ms[3], launches[3])
-    apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, phase_ms[3], launches[3])
+    apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
+    apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
+    apsp_set_int32_arith(mode), apsp_get_int32_arith()
     apsp_pivot_block(n), apsp_status_string(s), apsp_last_hip_error(), apsp_version()
 
 Tensor convenience:
     fw(t, inf=None)              in-place APSP of a 2-D int32/float32 CUDA tensor
     fw_rounds(t, r0, r1, inf=None)
-    fw_timed(t, inf=None)        -> (phase_ms, launches), synchronised
+    fw_timed(t, inf=None)        -> (phase_ms, launches, arith), synchronised
 """
 from __future__ import annotations
 
@@ -32,12 +33,17 @@ APSP_ERR_INVALID_VALUE = 1
 APSP_ERR_NO_DEVICE = 2
 APSP_ERR_LAUNCH = 3
 
+APSP_ARITH_AUTO = 0
+APSP_ARITH_F32_WHEN_EXACT = 1
+APSP_ARITH_INT32 = 2
+
 INF_I32 = 0x3FFFFFFF
 
 # Every symbol that include/apsp.h declares.
 EXPORTS = (
     "apsp_fw_i32", "apsp_fw_f32", "apsp_fw_rounds_i32", "apsp_fw_rounds_f32",
-    "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_pivot_block",
+    "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_set_int32_arith",
+    "apsp_get_int32_arith", "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
 )
 
@@ -74,13 +80,16 @@ def load(path: str | None = None):
     lib = ctypes.CDLL(p)
     i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     dp, lp = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+    ip = ctypes.POINTER(ctypes.c_int)
     sig = {
         "apsp_fw_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_f32": ([vp, i64, i64, f32, vp], ctypes.c_int),
         "apsp_fw_rounds_i32": ([vp, i64, i64, i32, i64, i64, vp], ctypes.c_int),
         "apsp_fw_rounds_f32": ([vp, i64, i64, f32, i64, i64, vp], ctypes.c_int),
-        "apsp_fw_timed_i32": ([vp, i64, i64, i32, vp, dp, lp], ctypes.c_int),
-        "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp], ctypes.c_int),
+        "apsp_fw_timed_i32": ([vp, i64, i64, i32, vp, dp, lp, ip], ctypes.c_int),
+        "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
+        "apsp_set_int32_arith": ([ctypes.c_int], ctypes.c_int),
+        "apsp_get_int32_arith": ([], ctypes.c_int),
         "apsp_pivot_block": ([i64], i64),
         "apsp_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "apsp_last_hip_error": ([], ctypes.c_int),
@@ -114,10 +123,11 @@ def apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream=0) -> int:
 
 
 def _timed(fn, d_ptr, n, ld, inf, stream):
-    ms = (ctypes.c_double * 3)()
-    cnt = (ctypes.c_int64 * 3)()
-    st = fn(d_ptr or None, n, ld, inf, stream or None, ms, cnt)
-    return st, list(ms), list(cnt)
+    ms = (ctypes.c_double * 4)()
+    cnt = (ctypes.c_int64 * 4)()
+    arith = ctypes.c_int(-1)
+    st = fn(d_ptr or None, n, ld, inf, stream or None, ms, cnt, ctypes.byref(arith))
+    return st, list(ms), list(cnt), int(arith.value)
 
 
 def apsp_fw_timed_i32(d_ptr, n, ld, inf, stream=0):
@@ -126,6 +136,31 @@ def apsp_fw_timed_i32(d_ptr, n, ld, inf, stream=0):
 
 def apsp_fw_timed_f32(d_ptr, n, ld, inf, stream=0):
     return _timed(load().apsp_fw_timed_f32, d_ptr, n, ld, inf, stream)
+
+
+def apsp_set_int32_arith(mode: int) -> int:
+    return int(load().apsp_set_int32_arith(mode))
+
+
+def apsp_get_int32_arith() -> int:
+    return int(load().apsp_get_int32_arith())
+
+
+class int32_arith:
+    """Context manager: run int32 calls under an arithmetic policy."""
+
+    def __init__(self, mode: int):
+        self.mode = mode
+
+    def __enter__(self):
+        self.prev = apsp_get_int32_arith()
+        if apsp_set_int32_arith(self.mode) != APSP_OK:
+            raise ValueError(f"bad arithmetic policy {self.mode}")
+        return self
+
+    def __exit__(self, *exc):
+        apsp_set_int32_arith(self.prev)
+        return False
 
 
 def apsp_pivot_block(n: int = 0) -> int:
@@ -192,10 +227,13 @@ def fw_rounds(t, r0, r1, inf=None):
 
 
 def fw_timed(t, inf=None):
+    """Like fw, synchronised; returns (ms per kind, launches per kind, arith)
+    with kinds [Phase 1, Phase 2, Phase 3, scan/convert] and arith 1 when the
+    call computed in binary32."""
     import torch
     kind, p, n, ld, inf, s = _tensor_args(t, inf)
     with torch.cuda.device(t.device):
-        st, ms, cnt = (apsp_fw_timed_i32 if kind == "i32" else apsp_fw_timed_f32)(p, n, ld, inf, s)
+        st, ms, cnt, arith = (apsp_fw_timed_i32 if kind == "i32" else apsp_fw_timed_f32)(p, n, ld, inf, s)
     if st != APSP_OK:
         raise APSPError(st, "apsp_fw_timed_" + kind)
-    return ms, cnt
+    return ms, cnt, arith

@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "apsp.h"
 
@@ -59,6 +60,7 @@ constexpr int kKC = APSP_KC;   // pivots per LDS chunk
 constexpr int kPad = 4;        // LDS row padding (elements), keeps 16-B alignment
 constexpr int kWavesP3 = 2;    // waves per SIMD targeted by Phase 3 (<= 256 VGPRs)
 constexpr int kWavesP2 = 4;    // waves per SIMD targeted by Phase 2 (<= 128 VGPRs)
+constexpr int kP3PerCu = 2;    // Phase-3 workgroups resident per CU
 
 // ---------------------------------------------------------------------------
 // Element operations.  int32: wrap-free because every value is <= inf <=
@@ -443,9 +445,8 @@ __device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds)
 
 // Standalone Phase 1 (first round of a call).
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
-                                                      T inf, int64_t K) {
-  __shared__ __attribute__((aligned(16))) T lds[kLdsClose];
+__device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                            int64_t K, T* __restrict__ lds) {
   const int64_t base = K * kB;
   T acc[8][8];
   if (base + kB <= n) {
@@ -463,9 +464,8 @@ __global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t
 // Phase 2: pivot-row tiles (blocks 0 .. nr-1) then pivot-column tiles.
 // ---------------------------------------------------------------------------
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
-fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb) {
-  __shared__ __attribute__((aligned(16))) T lds[kLdsP2];
+__device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                            int64_t K, int64_t nb, T* __restrict__ lds) {
   constexpr int kSub = kB / kP2;
   const int64_t nr = (nb - 1) * kSub;
   int64_t b = blockIdx.x;
@@ -520,9 +520,9 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
 }
 
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
-fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next) {
-  __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
+__device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                            int64_t K, int64_t nb, int fuse_next,
+                                            T* __restrict__ lds) {
   const uint32_t m = (uint32_t)(nb - 1);
   const uint32_t total = m * m;
   const uint32_t b = blockIdx.x;
@@ -555,13 +555,185 @@ fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb
 }
 
 // ---------------------------------------------------------------------------
+// int32 matrices in binary32 arithmetic.
+//
+// gfx950 issues binary32 adds and mins at twice the rate of int32 adds and
+// mins, so an int32 matrix is computed in binary32 whenever that is exact.
+// It is exact when every finite entry is an integer in [0, 2^24] and every
+// shortest distance -- and every distance restricted to intermediate vertices
+// below some pivot, which bounds each value the blocked recurrence stores --
+// is at most 2^24.  Then each value the recurrence keeps is the exact integer
+// (a candidate that realises a value <= 2^24 sums two exact values whose
+// exact sum is representable; any other candidate is >= that value even
+// after rounding, since rounding is monotone and 2^24 is representable).
+// The distance bound holds when no off-diagonal entry is inf (each distance
+// is at most the direct edge, hence at most the largest weight), or when
+// (n - 1) times the largest finite weight is at most 2^24 (a shortest path
+// is simple).  A scan kernel records the largest finite entry and two flags
+// in a small stream-ordered scratch; every later kernel of the call reads
+// them and takes the binary32 or the int32 body.  Entries equal to inf
+// become +infinity and come back as inf; finite results are clamped to inf,
+// which is what int32 arithmetic would store when a sum is not below inf.
+// ---------------------------------------------------------------------------
+constexpr int32_t kFlagHasInf = 1;     // some off-diagonal entry equals inf
+constexpr int32_t kFlagNotExact = 2;   // a negative entry, or a finite one above 2^24
+constexpr int64_t kExactLimit = int64_t(1) << 24;
+constexpr int kScanBlocks = 2048;
+
+__device__ __forceinline__ bool f32_exact(const int32_t* __restrict__ s, int64_t n) {
+  if (s == nullptr) return false;
+  const int32_t maxw = s[0];
+  const int32_t flags = s[1];
+  if (flags & kFlagNotExact) return false;
+  if (!(flags & kFlagHasInf)) return true;
+  return (n - 1) * (int64_t)maxw <= kExactLimit;
+}
+
+__global__ void __launch_bounds__(64) scan_zero(int32_t* __restrict__ s) {
+  if (threadIdx.x < 2) s[threadIdx.x] = 0;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) scan_i32(const int32_t* __restrict__ d, int64_t n,
+                                                     int64_t ld, int32_t inf,
+                                                     int32_t* __restrict__ s) {
+  int32_t mx = 0, fl = 0;
+  auto visit = [&](int32_t v, int64_t r, int64_t c) {
+    if (v == inf) {
+      if (r != c) fl |= kFlagHasInf;
+    } else {
+      if (v < 0 || v > kExactLimit) fl |= kFlagNotExact;
+      mx = max(mx, v);
+    }
+  };
+  const int64_t quads = (n + 3) / 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int32_t* row = d + r * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t c = q * 4;
+      if (VEC && c + 3 < n) {
+        int32_t v[4];
+        load4(row + c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) visit(v[e], r, c + e);
+      } else {
+        for (int e = 0; e < 4 && c + e < n; ++e) visit(row[c + e], r, c + e);
+      }
+    }
+  }
+  // wave reduction, then one atomic pair per wave
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o));
+    fl |= __shfl_xor(fl, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&s[0], mx);
+    atomicOr(&s[1], fl);
+  }
+}
+
+// In place: int32 bit patterns <-> binary32 bit patterns (only when exact).
+template <bool VEC, bool TO_F32>
+__global__ void __launch_bounds__(kThreads) convert_i32(int32_t* __restrict__ d, int64_t n,
+                                                        int64_t ld, int32_t inf,
+                                                        const int32_t* __restrict__ s) {
+  if (!f32_exact(s, n)) return;
+  const float finf = (float)inf;
+  auto conv = [&](int32_t v) -> int32_t {
+    if (TO_F32) return __float_as_int(v == inf ? __builtin_inff() : (float)v);
+    const float f = __int_as_float(v);
+    return f >= finf ? inf : (int32_t)f;
+  };
+  const int64_t quads = (n + 3) / 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    int32_t* row = d + r * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t c = q * 4;
+      if (VEC && c + 3 < n) {
+        int32_t v[4];
+        load4(row + c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = conv(v[e]);
+        store4(row + c, v);
+      } else {
+        for (int e = 0; e < 4 && c + e < n; ++e) row[c + e] = conv(row[c + e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.  fw_phase* run one element type; fw_phase*_i32 serve int32
+// matrices and take the binary32 body when the call's scan says it is exact.
+// ---------------------------------------------------------------------------
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
+                                                      T inf, int64_t K) {
+  __shared__ __attribute__((aligned(16))) T lds[kLdsClose];
+  phase1_body<T, VEC>(d, n, ld, inf, K, lds);
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb) {
+  __shared__ __attribute__((aligned(16))) T lds[kLdsP2];
+  phase2_body<T, VEC>(d, n, ld, inf, K, nb, lds);
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
+fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next) {
+  __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
+  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, lds);
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) fw_phase1_i32(int32_t* __restrict__ d, int64_t n,
+                                                          int64_t ld, int32_t inf, int64_t K,
+                                                          const int32_t* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsClose];
+  if (f32_exact(s, n))
+    phase1_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K,
+                            reinterpret_cast<float*>(lds));
+  else
+    phase1_body<int32_t, VEC>(d, n, ld, inf, K, lds);
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+fw_phase2_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
+              const int32_t* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP2];
+  if (f32_exact(s, n))
+    phase2_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
+                            reinterpret_cast<float*>(lds));
+  else
+    phase2_body<int32_t, VEC>(d, n, ld, inf, K, nb, lds);
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
+fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
+              int fuse_next, const int32_t* __restrict__ s) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP3];
+  if (f32_exact(s, n))
+    phase3_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
+                            fuse_next, reinterpret_cast<float*>(lds));
+  else
+    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, lds);
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 thread_local int g_last_hip_error = 0;
+std::atomic<int> g_int32_arith{APSP_ARITH_AUTO};
 
 // Per-device cache: 0 = unknown, 1 = gfx950, 2 = other.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
 
 int check_device() {
   int dev = 0;
@@ -576,8 +748,21 @@ int check_device() {
   const char* a = prop.gcnArchName;
   const bool ok = a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
                   a[5] == '0' && (a[6] == '\0' || a[6] == ':');
-  if (dev < kMaxDevices) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (dev < kMaxDevices) {
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  }
   return ok ? APSP_OK : APSP_ERR_NO_DEVICE;
+}
+
+// Compute units of the current device (known once check_device succeeded).
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    const int c = g_dev_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  return 256;
 }
 
 template <typename T>
@@ -600,45 +785,27 @@ int validate(const T* d, int64_t n, int64_t ld, T inf) {
   return APSP_OK;
 }
 
+// Launch kinds reported by the timed entry points.
+enum { kKindPhase1 = 0, kKindPhase2 = 1, kKindPhase3 = 2, kKindConvert = 3, kKinds = 4 };
+
 struct PhaseTimer {
   // Events bracketing each launch: ev[2*i] before, ev[2*i+1] after launch i.
   hipEvent_t* ev = nullptr;
-  int* phase = nullptr;
+  int* kind = nullptr;
   int64_t cap = 0, used = 0;
+  hipStream_t s = nullptr;
+  void mark(int k, bool before) {
+    if (before) {
+      (void)hipEventRecord(ev[2 * used], s);
+      kind[used] = k;
+    } else {
+      (void)hipEventRecord(ev[2 * used + 1], s);
+      ++used;
+    }
+  }
 };
 
-template <typename T, bool VEC>
-int enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
-                   PhaseTimer* tm) {
-  const int64_t nb = (n + kB - 1) / kB;
-  auto mark = [&](int phase, bool before) {
-    if (!tm) return;
-    if (before) {
-      (void)hipEventRecord(tm->ev[2 * tm->used], s);
-      tm->phase[tm->used] = phase;
-    } else {
-      (void)hipEventRecord(tm->ev[2 * tm->used + 1], s);
-      ++tm->used;
-    }
-  };
-  // Round r0 closes its diagonal block on its own; every later round's
-  // Phase 1 runs inside the previous round's Phase-3 launch.
-  mark(0, true);
-  hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
-  mark(0, false);
-  for (int64_t K = r0; K < r1 && nb > 1; ++K) {
-    const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
-    mark(1, true);
-    hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n, ld,
-                       inf, K, nb);
-    mark(1, false);
-    const int64_t g3 = (nb - 1) * (nb - 1);
-    const int fuse = K + 1 < r1 ? 1 : 0;
-    mark(2, true);
-    hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
-                       inf, K, nb, fuse);
-    mark(2, false);
-  }
+int launch_status() {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -647,9 +814,76 @@ int enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, h
   return APSP_OK;
 }
 
+// Rounds [r0, r1).  For int32 matrices `scratch` (may be null) holds the
+// scan result that selects binary32 or int32 arithmetic inside the kernels.
+template <typename T, bool VEC>
+void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
+                    const int32_t* scratch, PhaseTimer* tm) {
+  const int64_t nb = (n + kB - 1) / kB;
+  auto mark = [&](int k, bool before) {
+    if (tm) tm->mark(k, before);
+  };
+  // Round r0 closes its diagonal block on its own; every later round's
+  // Phase 1 runs inside the previous round's Phase-3 launch.
+  mark(kKindPhase1, true);
+  if constexpr (std::is_same_v<T, int32_t>)
+    hipLaunchKernelGGL((fw_phase1_i32<VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0,
+                       scratch);
+  else
+    hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
+  mark(kKindPhase1, false);
+  for (int64_t K = r0; K < r1 && nb > 1; ++K) {
+    const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
+    mark(kKindPhase2, true);
+    if constexpr (std::is_same_v<T, int32_t>)
+      hipLaunchKernelGGL((fw_phase2_i32<VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n,
+                         ld, inf, K, nb, scratch);
+    else
+      hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n, ld,
+                         inf, K, nb);
+    mark(kKindPhase2, false);
+    const int64_t g3 = (nb - 1) * (nb - 1);
+    const int fuse = K + 1 < r1 ? 1 : 0;
+    mark(kKindPhase3, true);
+    if constexpr (std::is_same_v<T, int32_t>)
+      hipLaunchKernelGGL((fw_phase3_i32<VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n,
+                         ld, inf, K, nb, fuse, scratch);
+    else
+      hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
+                         inf, K, nb, fuse);
+    mark(kKindPhase3, false);
+  }
+}
+
+// Scan + conversion around the rounds of an int32 call.
+template <bool VEC>
+void enqueue_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t r0, int64_t r1,
+                 hipStream_t s, int32_t* scratch, PhaseTimer* tm) {
+  const int64_t rows = n < kScanBlocks ? n : kScanBlocks;
+  if (scratch) {
+    if (tm) tm->mark(kKindConvert, true);
+    hipLaunchKernelGGL(scan_zero, dim3(1), dim3(64), 0, s, scratch);
+    hipLaunchKernelGGL((scan_i32<VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n, ld, inf,
+                       scratch);
+    hipLaunchKernelGGL((convert_i32<VEC, true>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n,
+                       ld, inf, scratch);
+    if (tm) tm->mark(kKindConvert, false);
+  }
+  enqueue_rounds<int32_t, VEC>(d, n, ld, inf, r0, r1, s, scratch, tm);
+  if (scratch) {
+    if (tm) tm->mark(kKindConvert, true);
+    hipLaunchKernelGGL((convert_i32<VEC, false>), dim3((unsigned)rows), dim3(kThreads), 0, s, d,
+                       n, ld, inf, scratch);
+    if (tm) tm->mark(kKindConvert, false);
+  }
+}
+
+// Validates, then enqueues rounds [r0, r1).  For int32 the scan result is
+// copied to scan_out (host, when non-null; valid after the stream has
+// synchronised) before the stream-ordered scratch is released.
 template <typename T>
 int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream,
-        PhaseTimer* tm) {
+        PhaseTimer* tm, int32_t* scan_out) {
   int st = validate<T>(d, n, ld, inf);
   if (st != APSP_OK) return st;
   const int64_t nb = n == 0 ? 0 : (n + kB - 1) / kB;
@@ -658,39 +892,87 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
   st = check_device();
   if (st != APSP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (tm) tm->s = s;
   const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
-  return vec ? enqueue_rounds<T, true>(d, n, ld, inf, r0, r1, s, tm)
-             : enqueue_rounds<T, false>(d, n, ld, inf, r0, r1, s, tm);
+  if constexpr (std::is_same_v<T, int32_t>) {
+    // Binary32 pays only when Phase 3 keeps two workgroups on every CU (its
+    // double issue rate needs two waves per SIMD); smaller matrices stay in
+    // int32 and skip the scan.  The scan result lives in a few bytes of
+    // stream-ordered scratch; without it the call stays in int32.
+    int32_t* scratch = nullptr;
+    const int64_t tiles = (nb - 1) * (nb - 1);
+    const int policy = g_int32_arith.load(std::memory_order_relaxed);
+    const bool try_f32 = policy == APSP_ARITH_F32_WHEN_EXACT ||
+                         (policy == APSP_ARITH_AUTO && tiles >= (int64_t)kP3PerCu * device_cus());
+    if (try_f32) {
+      if (hipMallocAsync(reinterpret_cast<void**>(&scratch), 256, s) != hipSuccess) {
+        scratch = nullptr;
+        (void)hipGetLastError();
+      }
+    }
+    if (vec) enqueue_i32<true>(d, n, ld, inf, r0, r1, s, scratch, tm);
+    else enqueue_i32<false>(d, n, ld, inf, r0, r1, s, scratch, tm);
+    if (scratch) {
+      if (scan_out)
+        (void)hipMemcpyAsync(scan_out, scratch, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+      (void)hipFreeAsync(scratch, s);
+    }
+  } else {
+    (void)scan_out;
+    if (vec) enqueue_rounds<T, true>(d, n, ld, inf, r0, r1, s, nullptr, tm);
+    else enqueue_rounds<T, false>(d, n, ld, inf, r0, r1, s, nullptr, tm);
+  }
+  return launch_status();
+}
+
+// Timing events are created once per thread and device and reused, so the
+// measured calls do not pay for event creation.  Timing-only events carry
+// no system-scope fence (no cache writeback between the kernels they
+// bracket).  They live until the process ends.
+struct EventPool {
+  hipEvent_t* ev = nullptr;
+  int64_t size = 0;
+};
+thread_local EventPool g_event_pool[kMaxDevices];
+
+hipEvent_t* pooled_events(int64_t count) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  EventPool& p = g_event_pool[dev];
+  if (p.size >= count) return p.ev;
+  hipEvent_t* ev = new hipEvent_t[count];
+  for (int64_t i = 0; i < p.size; ++i) ev[i] = p.ev[i];
+  int64_t made = p.size;
+  for (; made < count; ++made)
+    if (hipEventCreateWithFlags(&ev[made], hipEventDisableSystemFence) != hipSuccess) break;
+  delete[] p.ev;
+  p.ev = ev;
+  p.size = made;
+  return made >= count ? ev : nullptr;
 }
 
 template <typename T>
 int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms,
-              int64_t* phase_launch) {
+              int64_t* phase_launch, int* arith) {
   int st = validate<T>(d, n, ld, inf);
   if (st != APSP_OK) return st;
-  if (phase_ms) for (int p = 0; p < 3; ++p) phase_ms[p] = 0.0;
-  if (phase_launch) for (int p = 0; p < 3; ++p) phase_launch[p] = 0;
+  if (phase_ms) for (int p = 0; p < kKinds; ++p) phase_ms[p] = 0.0;
+  if (phase_launch) for (int p = 0; p < kKinds; ++p) phase_launch[p] = 0;
+  if (arith) *arith = std::is_same_v<T, int32_t> ? 0 : 1;
   if (n == 0) return APSP_OK;
   st = check_device();
   if (st != APSP_OK) return st;
   const int64_t nb = (n + kB - 1) / kB;
   PhaseTimer tm;
-  tm.cap = 3 * nb;
-  tm.ev = new hipEvent_t[2 * tm.cap];
-  tm.phase = new int[tm.cap];
-  int64_t created = 0;
-  // Timing-only events: no system-scope fence (no cache writeback between
-  // the kernels they bracket).
-  for (; created < 2 * tm.cap; ++created)
-    if (hipEventCreateWithFlags(&tm.ev[created], hipEventDisableSystemFence) != hipSuccess) break;
-  if (created < 2 * tm.cap) {
-    for (int64_t i = 0; i < created; ++i) (void)hipEventDestroy(tm.ev[i]);
-    delete[] tm.ev;
-    delete[] tm.phase;
+  tm.cap = 3 * nb + 4;
+  tm.ev = pooled_events(2 * tm.cap);
+  if (tm.ev == nullptr) {
     g_last_hip_error = (int)hipGetLastError();
     return APSP_ERR_LAUNCH;
   }
-  st = run<T>(d, n, ld, inf, 0, nb, stream, &tm);
+  tm.kind = new int[tm.cap];
+  int32_t scan[2] = {0, -1};
+  st = run<T>(d, n, ld, inf, 0, nb, stream, &tm, scan);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(s) != hipSuccess && st == APSP_OK) {
     g_last_hip_error = (int)hipGetLastError();
@@ -700,14 +982,18 @@ int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms
     for (int64_t i = 0; i < tm.used; ++i) {
       float ms = 0.f;
       (void)hipEventElapsedTime(&ms, tm.ev[2 * i], tm.ev[2 * i + 1]);
-      const int p = tm.phase[i];
+      const int p = tm.kind[i];
       if (phase_ms) phase_ms[p] += ms;
       if (phase_launch) phase_launch[p] += 1;
     }
+    if (arith && std::is_same_v<T, int32_t>) {
+      // Same decision the kernels took (see f32_exact).
+      const bool exact = scan[1] >= 0 && !(scan[1] & kFlagNotExact) &&
+                         (!(scan[1] & kFlagHasInf) || (n - 1) * (int64_t)scan[0] <= kExactLimit);
+      *arith = exact ? 1 : 0;
+    }
   }
-  for (int64_t i = 0; i < 2 * tm.cap; ++i) (void)hipEventDestroy(tm.ev[i]);
-  delete[] tm.ev;
-  delete[] tm.phase;
+  delete[] tm.kind;
   return st;
 }
 
@@ -717,33 +1003,42 @@ extern "C" {
 
 int apsp_fw_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream) {
   const int64_t nb = n > 0 ? (n + kB - 1) / kB : 0;
-  return run<int32_t>(d, n, ld, inf, 0, nb, stream, nullptr);
+  return run<int32_t>(d, n, ld, inf, 0, nb, stream, nullptr, nullptr);
 }
 
 int apsp_fw_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
   const int64_t nb = n > 0 ? (n + kB - 1) / kB : 0;
-  return run<float>(d, n, ld, inf, 0, nb, stream, nullptr);
+  return run<float>(d, n, ld, inf, 0, nb, stream, nullptr, nullptr);
 }
 
 int apsp_fw_rounds_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t round_begin,
                        int64_t round_end, void* stream) {
-  return run<int32_t>(d, n, ld, inf, round_begin, round_end, stream, nullptr);
+  return run<int32_t>(d, n, ld, inf, round_begin, round_end, stream, nullptr, nullptr);
 }
 
 int apsp_fw_rounds_f32(float* d, int64_t n, int64_t ld, float inf, int64_t round_begin,
                        int64_t round_end, void* stream) {
-  return run<float>(d, n, ld, inf, round_begin, round_end, stream, nullptr);
+  return run<float>(d, n, ld, inf, round_begin, round_end, stream, nullptr, nullptr);
 }
 
 int apsp_fw_timed_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream,
-                      double* phase_ms, int64_t* phase_launch) {
-  return run_timed<int32_t>(d, n, ld, inf, stream, phase_ms, phase_launch);
+                      double* phase_ms, int64_t* phase_launch, int* arith) {
+  return run_timed<int32_t>(d, n, ld, inf, stream, phase_ms, phase_launch, arith);
 }
 
 int apsp_fw_timed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream,
-                      double* phase_ms, int64_t* phase_launch) {
-  return run_timed<float>(d, n, ld, inf, stream, phase_ms, phase_launch);
+                      double* phase_ms, int64_t* phase_launch, int* arith) {
+  return run_timed<float>(d, n, ld, inf, stream, phase_ms, phase_launch, arith);
 }
+
+int apsp_set_int32_arith(int mode) {
+  if (mode != APSP_ARITH_AUTO && mode != APSP_ARITH_F32_WHEN_EXACT && mode != APSP_ARITH_INT32)
+    return APSP_ERR_INVALID_VALUE;
+  g_int32_arith.store(mode, std::memory_order_relaxed);
+  return APSP_OK;
+}
+
+int apsp_get_int32_arith(void) { return g_int32_arith.load(std::memory_order_relaxed); }
 
 int64_t apsp_pivot_block(int64_t n) {
   (void)n;

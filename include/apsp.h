@@ -29,10 +29,21 @@
  * units in the last place per path edge of the exact real-number distances,
  * and bit-identical from run to run.
  *
- * Ownership and concurrency: the caller owns d.  The library allocates no
- * device memory and keeps no state beyond a per-device "is gfx950" cache, so
- * calls on different streams with different matrices may run concurrently.
- * Work is enqueued asynchronously on `stream`; the caller synchronises.
+ * Ownership and concurrency: the caller owns d.  An int32 call takes 256
+ * bytes of stream-ordered scratch (hipMallocAsync / hipFreeAsync on
+ * `stream`); float32 calls allocate nothing.  Beyond that the library keeps
+ * only a per-device "is gfx950" cache, so calls on different streams with
+ * different matrices may run concurrently.  Work is enqueued asynchronously
+ * on `stream`; the caller synchronises.
+ *
+ * Arithmetic of int32 calls: when every finite entry is an integer in
+ * [0, 2^24] and either no off-diagonal entry equals inf or (n - 1) times the
+ * largest finite entry is at most 2^24, every value the recurrence stores is
+ * an integer of at most 2^24, so the kernels compute in binary32, which is
+ * exact there and twice as fast on gfx950; the matrix is converted in place
+ * and back within the call.  Otherwise they compute in int32.  A scan kernel
+ * makes this choice on the device (no host synchronisation), and the
+ * results are identical either way (see apsp_set_int32_arith).
  *
  * Errors: argument errors return APSP_ERR_INVALID_VALUE before any HIP call
  * (nothing is enqueued, d is untouched).  A current device that is not
@@ -90,18 +101,33 @@ int apsp_fw_rounds_f32(float *d, int64_t n, int64_t ld, float inf,
 
 /*
  * Measurement variant of apsp_fw_i32 / apsp_fw_f32: the same kernels on
- * the same stream, with HIP events recorded around each phase's launch.
- * It synchronises the stream before returning and writes:
+ * the same stream, with HIP events recorded around each launch (or group
+ * of launches).  It synchronises the stream before returning and writes:
  *   phase_ms[p]     summed event time of the launches of kind p, in ms;
- *   phase_launch[p] number of launches of kind p;
- * kinds: 0 = standalone Phase 1 (first round only), 1 = Phase 2,
- * 2 = Phase 3 (which also carries the next round's Phase 1).
- * Either pointer may be NULL.  Errors as for apsp_fw_i32.
+ *   phase_launch[p] number of timed launches (or groups) of kind p;
+ *   *arith          1 if the call computed in binary32, 0 if in int32;
+ * kinds (arrays of 4): 0 = standalone Phase 1 (first round only),
+ * 1 = Phase 2, 2 = Phase 3 (which also carries the next round's Phase 1),
+ * 3 = the int32 scan and the in-place conversions (one group before the
+ * rounds, one after).  Any pointer may be NULL.  Errors as for apsp_fw_i32.
  */
 int apsp_fw_timed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream,
-                      double *phase_ms, int64_t *phase_launch);
+                      double *phase_ms, int64_t *phase_launch, int *arith);
 int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
-                      double *phase_ms, int64_t *phase_launch);
+                      double *phase_ms, int64_t *phase_launch, int *arith);
+
+/*
+ * Arithmetic policy of int32 calls (process-wide; affects calls made after
+ * it is set).  APSP_ARITH_AUTO (default): binary32 when it is exact (see
+ * above) and Phase 3 has at least two 128 x 128 tiles per compute unit,
+ * since binary32's double issue rate needs two waves per SIMD; otherwise
+ * int32.  APSP_ARITH_F32_WHEN_EXACT: binary32 whenever it is exact.
+ * APSP_ARITH_INT32: always int32.  Results are identical under every
+ * policy.  Returns APSP_ERR_INVALID_VALUE for an unknown mode.
+ */
+enum { APSP_ARITH_AUTO = 0, APSP_ARITH_F32_WHEN_EXACT = 1, APSP_ARITH_INT32 = 2 };
+int apsp_set_int32_arith(int mode);
+int apsp_get_int32_arith(void);
 
 /* Pivot block edge B used for an n-vertex matrix (rounds = ceil(n / B)). */
 int64_t apsp_pivot_block(int64_t n);

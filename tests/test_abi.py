@@ -83,6 +83,14 @@ def test_round_range_errors(lib):
     assert ga.apsp_fw_rounds_f32(FAKE, 300, 300, 1.0, 0, 4) == ga.APSP_ERR_INVALID_VALUE
 
 
+def test_arith_policy_setter(lib):
+    assert ga.apsp_get_int32_arith() == ga.APSP_ARITH_AUTO
+    assert ga.apsp_set_int32_arith(7) == ga.APSP_ERR_INVALID_VALUE
+    with ga.int32_arith(ga.APSP_ARITH_INT32):
+        assert ga.apsp_get_int32_arith() == ga.APSP_ARITH_INT32
+    assert ga.apsp_get_int32_arith() == ga.APSP_ARITH_AUTO
+
+
 def test_empty_is_a_no_op(lib):
     assert ga.apsp_fw_i32(0, 0, 1, 100, 0) == ga.APSP_OK
     assert ga.apsp_fw_f32(0, 0, 1, 1.0, 0) == ga.APSP_OK
@@ -90,8 +98,10 @@ def test_empty_is_a_no_op(lib):
 
 
 def test_timed_variant_validates_too(lib):
-    st, ms, cnt = ga.apsp_fw_timed_i32(0, 4, 4, 100)
-    assert st == ga.APSP_ERR_INVALID_VALUE and cnt == [0, 0, 0] or st == ga.APSP_ERR_INVALID_VALUE
+    st, ms, cnt, arith = ga.apsp_fw_timed_i32(0, 4, 4, 100)
+    assert st == ga.APSP_ERR_INVALID_VALUE
+    st, ms, cnt, arith = ga.apsp_fw_timed_f32(FAKE, 4, 3, 1.0)
+    assert st == ga.APSP_ERR_INVALID_VALUE
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -76,12 +76,18 @@ def family(name, n, seed):
     raise KeyError(name)
 
 
+ARITH = {"auto": ga.APSP_ARITH_AUTO, "f32": ga.APSP_ARITH_F32_WHEN_EXACT,
+         "i32": ga.APSP_ARITH_INT32}
+
+
 @pytest.mark.parametrize("n", SIZES)
 @pytest.mark.parametrize("fam", ["er", "complete", "ring", "two_rings"])
-def test_int32_sweep(torch_dev, n, fam):
-    print(f"case int32 {fam} n={n}", flush=True)
+@pytest.mark.parametrize("arith", ["auto", "f32"])
+def test_int32_sweep(torch_dev, n, fam, arith):
+    print(f"case int32 {fam} n={n} arith={arith}", flush=True)
     w = family(fam, n, 100 + n)
-    got = gpu_apsp(torch_dev, w, INF)
+    with ga.int32_arith(ARITH[arith]):
+        got = gpu_apsp(torch_dev, w, INF)
     assert np.array_equal(got, oracle.fw_i32(w))
 
 
@@ -183,11 +189,96 @@ def test_timed_variant_counts_launches(torch_dev):
     n = 1000
     w = gg.erdos_renyi(n, 0.01, 1, 100, 5)
     t = torch.from_numpy(w).to(dev)
-    ms, cnt = ga.fw_timed(t, INF)
     nb = (n + 127) // 128
-    assert cnt == [1, nb, nb]   # later Phase 1s run inside Phase-3 launches
+    with ga.int32_arith(ga.APSP_ARITH_F32_WHEN_EXACT):
+        ms, cnt, arith = ga.fw_timed(t, INF)
+    # later Phase 1s run inside Phase-3 launches; scan+convert timed as 2 groups
+    assert cnt == [1, nb, nb, 2]
     assert all(x > 0 for x in ms)
+    assert arith == 1            # 999 * 100 <= 2^24: binary32 arithmetic
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+    t = torch.from_numpy(w).to(dev)
+    ms, cnt, arith = ga.fw_timed(t, INF)   # auto: too few tiles for binary32
+    assert cnt == [1, nb, nb, 0] and arith == 0
+    assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+    wf = gg.complete_f32(300, 3)
+    tf = torch.from_numpy(wf).to(dev)
+    ms, cnt, arith = ga.fw_timed(tf)
+    assert cnt == [1, 3, 3, 0] and arith == 1
+
+
+# ---- int32 matrices: binary32 vs int32 arithmetic --------------------------
+
+LIM = 1 << 24
+
+
+def _arith_of(torch_dev, w, inf, mode=ga.APSP_ARITH_F32_WHEN_EXACT):
+    torch, dev = torch_dev
+    t = torch.from_numpy(w).to(dev)
+    with ga.int32_arith(mode):
+        _, _, arith = ga.fw_timed(t, inf)
+    return arith, t.cpu().numpy()
+
+
+def test_int32_policy_forces_int_arithmetic(torch_dev):
+    w = gg.complete(300, 1, 1000, 12)
+    arith, got = _arith_of(torch_dev, w, INF, ga.APSP_ARITH_INT32)
+    assert arith == 0 and np.array_equal(got, oracle.fw_i32(w))
+    arith, got = _arith_of(torch_dev, w, INF, ga.APSP_ARITH_F32_WHEN_EXACT)
+    assert arith == 1 and np.array_equal(got, oracle.fw_i32(w))
+
+
+def test_rounds_resume_in_binary32(torch_dev):
+    torch, dev = torch_dev
+    n = 300
+    w = gg.erdos_renyi(n, 0.02, 1, 100, 18)
+    t = torch.from_numpy(w).to(dev)
+    with ga.int32_arith(ga.APSP_ARITH_F32_WHEN_EXACT):
+        ga.fw_rounds(t, 0, 1, INF)
+        torch.cuda.synchronize()
+        assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w, k_end=128))
+        ga.fw_rounds(t, 1, 3, INF)
+        torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+
+
+@pytest.mark.parametrize("case", ["complete_at_limit", "ring_at_bound", "big_weights",
+                                  "ring_over_bound", "negative_free_small_inf",
+                                  "complete_over_limit"])
+def test_int32_arithmetic_choice_and_exactness(torch_dev, case):
+    print(f"case arith {case}", flush=True)
+    rng = np.random.default_rng(7)
+    if case == "complete_at_limit":          # weights up to 2^24, no inf: binary32
+        n = 300
+        w = rng.integers(LIM - 5000, LIM + 1, size=(n, n)).astype(np.int32)
+        np.fill_diagonal(w, 0)
+        want_arith = 1
+        inf = INF
+    elif case == "ring_at_bound":            # (n-1) * w == 2^24 exactly: binary32
+        n = 257
+        w = gg.ring(n, LIM // 256)
+        want_arith, inf = 1, INF
+    elif case == "ring_over_bound":          # (n-1) * w > 2^24 with inf: int32
+        n = 258
+        w = gg.ring(n, LIM // 256)
+        want_arith, inf = 0, INF
+    elif case == "big_weights":              # a weight above 2^24: int32
+        n = 200
+        w = gg.erdos_renyi(n, 0.05, 1, 100, 3)
+        w[3, 7] = (1 << 28) + 1
+        want_arith, inf = 0, INF
+    elif case == "negative_free_small_inf":  # small sentinel; sums may exceed it
+        n = 150
+        w = gg.erdos_renyi(n, 0.03, 1, 60, 9, inf=100)
+        want_arith, inf = 1, 100
+    else:                                    # complete, one weight 2^24 + 1: int32
+        n = 130
+        w = gg.complete(n, 1, 1000, 4)
+        w[5, 9] = LIM + 1
+        want_arith, inf = 0, INF
+    arith, got = _arith_of(torch_dev, w, inf)
+    assert arith == want_arith
+    assert np.array_equal(got, oracle.fw_i32(w)), case
 
 
 def test_tensor_wrapper_errors(torch_dev):

@@ -35,10 +35,13 @@ def run(torch_dev, w, inf):
 
 
 @pytest.mark.parametrize("name", ["er-256-p0.1-i32", "er-2048-p0.05-i32"])
-def test_small_workloads_full_oracle(torch_dev, name):
-    print(f"case workload {name}", flush=True)
+@pytest.mark.parametrize("arith", [ga.APSP_ARITH_AUTO, ga.APSP_ARITH_F32_WHEN_EXACT])
+def test_small_workloads_full_oracle(torch_dev, name, arith):
+    print(f"case workload {name} arith policy {arith}", flush=True)
     w = gg.make_workload(name)
-    assert np.array_equal(run(torch_dev, w, INF), oracle.fw_i32(w))
+    with ga.int32_arith(arith):
+        got = run(torch_dev, w, INF)
+    assert np.array_equal(got, oracle.fw_i32(w))
 
 
 def sample_sources(n, k, seed):
