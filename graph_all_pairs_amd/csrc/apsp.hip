@@ -621,15 +621,31 @@ __global__ void __launch_bounds__(kThreads) scan_i32(const int32_t* __restrict__
       }
     }
   }
-  // wave reduction, then one atomic pair per wave
+  // Workgroup reduction, then at most one atomic pair per workgroup: the
+  // stored values only grow, so a workgroup whose result is already covered
+  // by what it reads skips the atomic (thousands of workgroups would
+  // otherwise serialise on the same two words).
+  __shared__ int32_t red[2][kThreads / 64];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     mx = max(mx, __shfl_xor(mx, o));
     fl |= __shfl_xor(fl, o);
   }
   if ((threadIdx.x & 63) == 0) {
-    atomicMax(&s[0], mx);
-    atomicOr(&s[1], fl);
+    red[0][threadIdx.x / 64] = mx;
+    red[1][threadIdx.x / 64] = fl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      mx = max(mx, red[0][w]);
+      fl |= red[1][w];
+    }
+    const int32_t cur_mx = __hip_atomic_load(&s[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t cur_fl = __hip_atomic_load(&s[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (mx > cur_mx) atomicMax(&s[0], mx);
+    if (fl & ~cur_fl) atomicOr(&s[1], fl);
   }
 }
 
