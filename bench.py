@@ -212,6 +212,21 @@ def main() -> int:
         "launches": p3_launch,
     }
 
+    # Register-only replica of the Phase-3 inner step, both arithmetics.
+    ceilings = {}
+    for name, code in (("int32", 0), ("f32", 1)):
+        st_c, c = ga.apsp_minplus_ceiling(code)
+        if st_c == ga.APSP_OK:
+            ceilings[name] = c
+    if ceilings:
+        log("register-only min-plus ceilings (Trelax/s): "
+            + ", ".join(f"{k} {v / 1e12:.2f}" for k, v in ceilings.items()))
+    own = ceilings.get("int32" if arith == "int32" else "f32")
+    if own:
+        roofline["ceiling_measured"] = own / 1e12
+        roofline["frac_of_ceiling"] = achieved / own
+    roofline["ceilings_measured"] = {k: v / 1e12 for k, v in ceilings.items()}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -13,7 +13,7 @@ streams are integers):
     apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream) -> status
     apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
     apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
-    apsp_set_int32_arith(mode), apsp_get_int32_arith()
+    apsp_set_int32_arith(mode), apsp_get_int32_arith(), apsp_minplus_ceiling(arith)
     apsp_pivot_block(n), apsp_status_string(s), apsp_last_hip_error(), apsp_version()
 
 Tensor convenience:
@@ -43,7 +43,7 @@ INF_I32 = 0x3FFFFFFF
 EXPORTS = (
     "apsp_fw_i32", "apsp_fw_f32", "apsp_fw_rounds_i32", "apsp_fw_rounds_f32",
     "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_set_int32_arith",
-    "apsp_get_int32_arith", "apsp_pivot_block",
+    "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
 )
 
@@ -90,6 +90,7 @@ def load(path: str | None = None):
         "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
         "apsp_set_int32_arith": ([ctypes.c_int], ctypes.c_int),
         "apsp_get_int32_arith": ([], ctypes.c_int),
+        "apsp_minplus_ceiling": ([ctypes.c_int, dp], ctypes.c_int),
         "apsp_pivot_block": ([i64], i64),
         "apsp_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "apsp_last_hip_error": ([], ctypes.c_int),
@@ -161,6 +162,13 @@ class int32_arith:
     def __exit__(self, *exc):
         apsp_set_int32_arith(self.prev)
         return False
+
+
+def apsp_minplus_ceiling(arith: int):
+    """(status, relaxations/s) of the register-only min-plus core."""
+    r = ctypes.c_double(0.0)
+    st = load().apsp_minplus_ceiling(arith, ctypes.byref(r))
+    return int(st), float(r.value)
 
 
 def apsp_pivot_block(n: int = 0) -> int:

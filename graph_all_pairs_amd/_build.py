@@ -7,6 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "apsp.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "ceiling.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libapsp.so")
 ARCH = "gfx950"
@@ -27,9 +28,9 @@ def hipcc() -> str:
 
 
 def build_library(out: str = LIB_PATH, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile csrc/apsp.hip into ``out`` (always recompiles)."""
+    """Compile the csrc/ sources into ``out`` (always recompiles)."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *(extra or []), SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *(extra or []), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,95 @@
+// Empirical VALU ceiling of the min-plus core on the current device.
+//
+// A register-only replica of the Phase-3 inner step: each thread holds an
+// 8 x 8 block of accumulators and, per pair of pivots, forms two candidate
+// sums per accumulator and folds them in with one three-input min -- the
+// same add, add, min3 instruction mix and the same 2 waves per SIMD as the
+// tile kernel, but with operands already in registers (no LDS, no global
+// memory, no barriers).  Its rate is the most the tile kernel's instruction
+// stream can reach on this device, clock and occupancy, and is reported next
+// to the peak derived from unit counts and clock.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "apsp.h"
+
+namespace {
+
+__device__ __forceinline__ int32_t ceil_min3(int32_t a, int32_t b, int32_t c) {
+  int32_t r;
+  asm("v_min3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float ceil_min3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+minplus_core(T* __restrict__ out, int iters) {
+  T acc[8][8], a0[8], a1[8], b0[8], b1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a0[i] = (T)(threadIdx.x + i);
+    a1[i] = (T)(2 * threadIdx.x + i);
+    b0[i] = (T)(3 * i);
+    b1[i] = (T)(5 * i + 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = (T)(1000000 + 8 * i + j);
+  }
+  for (int it = 0; it < iters; ++it) {
+    // Opaque to the compiler: the sums cannot be hoisted out of the loop.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a0[i]), "+v"(a1[i]), "+v"(b0[i]), "+v"(b1[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = ceil_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+  }
+  T s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = s + acc[i][j];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+template <typename T>
+int measure(double* relax_per_s) {
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return APSP_ERR_NO_DEVICE;
+  const int blocks = 2 * prop.multiProcessorCount;  // 2 waves per SIMD
+  const int iters = 4000;
+  T* out = nullptr;
+  if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(T)) != hipSuccess) return APSP_ERR_LAUNCH;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int st = APSP_OK;
+  float ms = 0.f;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) st = APSP_ERR_LAUNCH;
+  if (st == APSP_OK) {
+    hipLaunchKernelGGL((minplus_core<T>), dim3(blocks), dim3(256), 0, 0, out, iters / 8);  // warm-up
+    (void)hipEventRecord(e0, 0);
+    hipLaunchKernelGGL((minplus_core<T>), dim3(blocks), dim3(256), 0, 0, out, iters);
+    (void)hipEventRecord(e1, 0);
+    if (hipEventSynchronize(e1) != hipSuccess || hipGetLastError() != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f)
+      st = APSP_ERR_LAUNCH;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(out);
+  if (st == APSP_OK && relax_per_s)
+    *relax_per_s = (double)blocks * 256.0 * iters * 128.0 / (ms * 1e-3);
+  return st;
+}
+
+}  // namespace
+
+extern "C" int apsp_minplus_ceiling(int arith, double* relax_per_s) {
+  if (relax_per_s == nullptr || (arith != 0 && arith != 1)) return APSP_ERR_INVALID_VALUE;
+  return arith == 1 ? measure<float>(relax_per_s) : measure<int32_t>(relax_per_s);
+}

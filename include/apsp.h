@@ -129,6 +129,17 @@ enum { APSP_ARITH_AUTO = 0, APSP_ARITH_F32_WHEN_EXACT = 1, APSP_ARITH_INT32 = 2 
 int apsp_set_int32_arith(int mode);
 int apsp_get_int32_arith(void);
 
+/*
+ * Diagnostic: the empirical VALU ceiling of the min-plus core on the current
+ * device, in relaxations per second.  Runs a register-only replica of the
+ * Phase-3 inner step (8 x 8 accumulators per thread, two candidates per
+ * three-input min, 2 waves per SIMD, no memory traffic) on the null stream
+ * and synchronises.  arith: 0 = int32 arithmetic, 1 = binary32.  Allocates
+ * and frees a small device buffer.  Returns APSP_ERR_INVALID_VALUE for a bad
+ * argument, APSP_ERR_LAUNCH on a HIP failure.
+ */
+int apsp_minplus_ceiling(int arith, double *relax_per_s);
+
 /* Pivot block edge B used for an n-vertex matrix (rounds = ceil(n / B)). */
 int64_t apsp_pivot_block(int64_t n);
 

@@ -289,3 +289,12 @@ def test_tensor_wrapper_errors(torch_dev):
         ga.fw(torch.zeros((4, 3), dtype=torch.int32, device=dev))
     with pytest.raises(ga.APSPError):
         ga.fw(torch.zeros((4, 4), dtype=torch.int32, device=dev), inf=0)
+
+
+def test_minplus_ceiling_diagnostic(torch_dev):
+    # the register-only core runs between half and twice the spec peaks
+    st, r32 = ga.apsp_minplus_ceiling(0)
+    assert st == ga.APSP_OK and 0.5 * 2.62e13 < r32 < 2.0 * 2.62e13
+    st, rf = ga.apsp_minplus_ceiling(1)
+    assert st == ga.APSP_OK and 0.5 * 5.24e13 < rf < 2.0 * 5.24e13
+    assert ga.apsp_minplus_ceiling(5)[0] == ga.APSP_ERR_INVALID_VALUE
