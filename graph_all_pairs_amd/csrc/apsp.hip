@@ -58,16 +58,23 @@ constexpr int kThreads = 256;  // Phase 2/3 workgroup size
 #endif
 constexpr int kKC = APSP_KC;   // pivots per LDS chunk
 constexpr int kPad = 4;        // LDS row padding (elements), keeps 16-B alignment
-constexpr int kWavesP3 = 2;    // waves per SIMD targeted by Phase 3 (<= 256 VGPRs)
+constexpr int kWavesP3 = 3;    // waves per SIMD targeted by Phase 3 (<= 168 VGPRs): a
+                               // third wave per SIMD keeps the VALU fed while the
+                               // others wait on LDS (measured faster than two waves
+                               // with software-pipelined operand reads)
 constexpr int kWavesP2 = 4;    // waves per SIMD targeted by Phase 2 (<= 128 VGPRs)
-constexpr int kP3PerCu = 2;    // Phase-3 workgroups resident per CU
+constexpr int kP3PerCu = 2;    // Phase-3 tiles per CU below which int32 calls stay in int32
 
 // ---------------------------------------------------------------------------
 // Element operations.  int32: wrap-free because every value is <= inf <=
 // 2^30 - 1.  float32: IEEE add and min (no NaN by precondition).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int32_t mp_min(int32_t a, int32_t b) { return min(a, b); }
-__device__ __forceinline__ float mp_min(float a, float b) { return fminf(a, b); }
+__device__ __forceinline__ float mp_min(float a, float b) {
+  float r;  // no NaN by precondition, so no canonicalising fminf
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 // min(a, b, c) as one v_min3.  Written as an instruction so that the compiler
 // keeps one three-input min per pair of candidates instead of re-balancing
@@ -350,20 +357,120 @@ using P2Col = TileShape<int32_t, kP2, kB, 4, 4>;
 using P3 = TileShape<int32_t, kB, kB, 8, 8>;
 constexpr int kLdsP2 = P2Row::kLdsElems > P2Col::kLdsElems ? P2Row::kLdsElems : P2Col::kLdsElems;
 constexpr int kLdsP3 = P3::kLdsElems;
-constexpr int kLdsClose = 4 * kB;  // pivot column + pivot row, two buffers each
+constexpr int kLdsClose = 8 * kB;  // two pivot columns + two pivot rows, two buffers
 
 // ---------------------------------------------------------------------------
 // Phase 1 on a kB x kB block held in registers in the 8 x 8 micro-tile layout
 // of a 256-thread workgroup (the Phase-3 layout): Floyd-Warshall over the
-// block's own pivots t = 0 .. kB-1, in order.  Before pivot t, the threads
-// owning column t and row t publish them to LDS (ping-pong buffers); pivot
-// row and column do not change during their own step (d[t][t] >= 0), so one
-// barrier per pivot orders everything.  Element updates are the page's
-// d <- min(d, d[x][t] + d[t][y]), in the same order as the plain recurrence,
-// so float results equal the sequential Floyd-Warshall on the block.
+// block's own pivots t = 0 .. kB-1, in order, two pivots per step.
+//
+// With D the block before pivot t, the plain recurrence gives after pivots t
+// and t+1
+//   D1[x][y] = min(D[x][y], D[x][t] + D[t][y])
+//   D2[x][y] = min(D1[x][y], D1[x][t+1] + D1[t+1][y])
+//            = min(D[x][y], D[x][t] + D[t][y], D1[x][t+1] + D1[t+1][y]),
+// and the only D1 values that takes are column t+1 and row t+1:
+//   D1[x][t+1] = min(D[x][t+1], D[x][t] + D[t][t+1]),
+//   D1[t+1][y] = min(D[t+1][y], D[t+1][t] + D[t][y]).
+// So a step publishes columns t, t+1 and rows t, t+1 of D to LDS, every
+// thread forms D1's column and row entries for its own 8 rows and 8 columns,
+// and each element takes one three-input min.  Every stored value is the
+// same expression, evaluated the same way, as in the one-pivot-at-a-time
+// recurrence, so float results equal the plain sequential Floyd-Warshall on
+// the block bit for bit.  Ping-pong LDS buffers: one barrier per pivot pair.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds) {
+  // lds: [2 buffers][4][kB] = column t, column t+1, row t, row t+1
+  const int tc = threadIdx.x % 16;
+  const int tr = threadIdx.x / 16;
+
+  // Pivot t = 64 g + 4 q + c lives in register slot s = 4 g + c of the
+  // threads with tc == q (its column) and tr == q (its row).
+  auto publish = [&](int buf, int owner, int slot) {
+    T* base = lds + buf * 4 * kB;
+    if (tc == owner) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        T v0[4] = {acc[0][slot + h], acc[1][slot + h], acc[2][slot + h], acc[3][slot + h]};
+        T v1[4] = {acc[4][slot + h], acc[5][slot + h], acc[6][slot + h], acc[7][slot + h]};
+        store4(&base[h * kB + tr * 4], v0);
+        store4(&base[h * kB + 64 + tr * 4], v1);
+      }
+    }
+    if (tr == owner) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        T v0[4] = {acc[slot + h][0], acc[slot + h][1], acc[slot + h][2], acc[slot + h][3]};
+        T v1[4] = {acc[slot + h][4], acc[slot + h][5], acc[slot + h][6], acc[slot + h][7]};
+        store4(&base[(2 + h) * kB + tc * 4], v0);
+        store4(&base[(2 + h) * kB + 64 + tc * 4], v1);
+      }
+    }
+  };
+
+  publish(0, 0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll 1
+    for (int q = 0; q < 16; ++q) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int t = 64 * g + 4 * q + 2 * cc;  // first pivot of the pair
+        const T* base = lds + cc * 4 * kB;      // pair index 32 g + 2 q + cc has parity cc
+        T a0[8], a1[8], b0[8], b1[8];
+        {
+          T v[4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            load4(&base[tr * 4 + 64 * h], v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a0[4 * h + i] = v[i];
+            load4(&base[kB + tr * 4 + 64 * h], v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a1[4 * h + i] = v[i];
+            load4(&base[2 * kB + tc * 4 + 64 * h], v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b0[4 * h + j] = v[j];
+            load4(&base[3 * kB + tc * 4 + 64 * h], v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b1[4 * h + j] = v[j];
+          }
+        }
+        const T d_t_t1 = base[2 * kB + t + 1];  // D[t][t+1]
+        const T d_t1_t = base[t + 1];           // D[t+1][t]
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a1[i] = mp_min(a1[i], a0[i] + d_t_t1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b1[j] = mp_min(b1[j], d_t1_t + b0[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = mp_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+
+        // publish the next pair into the other buffer
+        if (cc == 0) {
+          publish(1, q, 4 * g + 2);
+        } else if (q < 15) {
+          publish(0, q + 1, 4 * g);
+        } else if (g == 0) {
+          publish(0, 0, 4);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// The same closure one pivot per step (d <- min(d, d[x][t] + d[t][y]), one
+// barrier per pivot), for the next-round Phase 1 fused into the Phase-3
+// kernel.  There the pair-step version above made the Phase-3 tile loop
+// itself about 4 % slower (measured at n = 8192, also with the fused path
+// switched off, so the cost lies in the compiled kernel, not in the closure's
+// run time); the fused closure is off the critical path at large n.
+template <typename T>
+__device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ lds) {
   T* colv = lds;            // [2][kB]: column t at every row
   T* rowv = lds + 2 * kB;   // [2][kB]: row t at every column
   const int tc = threadIdx.x % 16;
@@ -545,11 +652,11 @@ __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_
   const bool interior = row0 + kB <= n && col0 + kB <= n && kb0 + kB <= n;
   if (interior) {
     minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc);
-    if (special) close_block<T>(acc, lds);
+    if (special) close_block_seq<T>(acc, lds);
     store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, row0, col0, acc);
   } else {
     minplus_update<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc);
-    if (special) close_block<T>(acc, lds);
+    if (special) close_block_seq<T>(acc, lds);
     store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, row0, col0, acc);
   }
 }
@@ -912,7 +1019,7 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
   const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
   if constexpr (std::is_same_v<T, int32_t>) {
     // Binary32 pays only when Phase 3 keeps two workgroups on every CU (its
-    // double issue rate needs two waves per SIMD); smaller matrices stay in
+    // double issue rate needs several waves per SIMD); smaller matrices stay in
     // int32 and skip the scan.  The scan result lives in a few bytes of
     // stream-ordered scratch; without it the call stays in int32.
     int32_t* scratch = nullptr;

@@ -3,11 +3,13 @@
 // A register-only replica of the Phase-3 inner step: each thread holds an
 // 8 x 8 block of accumulators and, per pair of pivots, forms two candidate
 // sums per accumulator and folds them in with one three-input min -- the
-// same add, add, min3 instruction mix and the same 2 waves per SIMD as the
-// tile kernel, but with operands already in registers (no LDS, no global
-// memory, no barriers).  Its rate is the most the tile kernel's instruction
-// stream can reach on this device, clock and occupancy, and is reported next
-// to the peak derived from unit counts and clock.
+// same add, add, min3 instruction mix as the tile kernel, but with operands
+// already in registers (no LDS, no global memory, no barriers).  It runs at
+// 2 and at 4 waves per SIMD and reports the faster: binary32's double issue
+// rate needs more than one wave per SIMD, and an odd wave count leaves part
+// of it unused, so this is the most the tile kernel's instruction stream can
+// reach on this device and clock.  It is reported next to the peak derived
+// from unit counts and clock.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,7 +29,7 @@ __device__ __forceinline__ float ceil_min3(float a, float b, float c) {
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 minplus_core(T* __restrict__ out, int iters) {
   T acc[8][8], a0[8], a1[8], b0[8], b1[8];
 #pragma unroll
@@ -57,12 +59,13 @@ minplus_core(T* __restrict__ out, int iters) {
 }
 
 template <typename T>
-int measure(double* relax_per_s) {
+int measure(int waves_per_simd, double* relax_per_s) {
   int dev = 0;
   hipDeviceProp_t prop;
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
     return APSP_ERR_NO_DEVICE;
-  const int blocks = 2 * prop.multiProcessorCount;  // 2 waves per SIMD
+  // A 256-thread workgroup puts one wave on each of a CU's 4 SIMDs.
+  const int blocks = waves_per_simd * prop.multiProcessorCount;
   const int iters = 4000;
   T* out = nullptr;
   if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(T)) != hipSuccess) return APSP_ERR_LAUNCH;
@@ -87,9 +90,22 @@ int measure(double* relax_per_s) {
   return st;
 }
 
+template <typename T>
+int measure_best(double* relax_per_s) {
+  double best = 0.0;
+  for (int w : {2, 4}) {
+    double r = 0.0;
+    const int st = measure<T>(w, &r);
+    if (st != APSP_OK) return st;
+    if (r > best) best = r;
+  }
+  *relax_per_s = best;
+  return APSP_OK;
+}
+
 }  // namespace
 
 extern "C" int apsp_minplus_ceiling(int arith, double* relax_per_s) {
   if (relax_per_s == nullptr || (arith != 0 && arith != 1)) return APSP_ERR_INVALID_VALUE;
-  return arith == 1 ? measure<float>(relax_per_s) : measure<int32_t>(relax_per_s);
+  return arith == 1 ? measure_best<float>(relax_per_s) : measure_best<int32_t>(relax_per_s);
 }

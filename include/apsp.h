@@ -120,7 +120,7 @@ int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
  * Arithmetic policy of int32 calls (process-wide; affects calls made after
  * it is set).  APSP_ARITH_AUTO (default): binary32 when it is exact (see
  * above) and Phase 3 has at least two 128 x 128 tiles per compute unit,
- * since binary32's double issue rate needs two waves per SIMD; otherwise
+ * since binary32's double issue rate needs several waves per SIMD; otherwise
  * int32.  APSP_ARITH_F32_WHEN_EXACT: binary32 whenever it is exact.
  * APSP_ARITH_INT32: always int32.  Results are identical under every
  * policy.  Returns APSP_ERR_INVALID_VALUE for an unknown mode.
@@ -133,8 +133,8 @@ int apsp_get_int32_arith(void);
  * Diagnostic: the empirical VALU ceiling of the min-plus core on the current
  * device, in relaxations per second.  Runs a register-only replica of the
  * Phase-3 inner step (8 x 8 accumulators per thread, two candidates per
- * three-input min, 2 waves per SIMD, no memory traffic) on the null stream
- * and synchronises.  arith: 0 = int32 arithmetic, 1 = binary32.  Allocates
+ * three-input min, no memory traffic) at 2 and at 4 waves per SIMD on the
+ * null stream, synchronises, and reports the faster rate.  arith: 0 = int32 arithmetic, 1 = binary32.  Allocates
  * and frees a small device buffer.  Returns APSP_ERR_INVALID_VALUE for a bad
  * argument, APSP_ERR_LAUNCH on a HIP failure.
  */
