@@ -14,6 +14,12 @@ Prints ONE JSON line:
   cpu_baseline the CPU oracle (plain Floyd-Warshall) timed on this host on a
                bounded sample of the same workload: its first k pivots
 
+With --workload batch-... (many independent graphs of n <= 128, see
+graphgen.BATCH_WORKLOADS) a step is one apsp_fw_batched_* call over the whole
+batch; value = batch * n^3 / (wall time per step), and the roofline entry
+describes the batched kernel (one launch per step, timed with events on its
+stream).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -30,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "APSP min-plus relaxations/s (n^3/time) at n=8192; % of VALU roofline"
+METRIC_BATCHED = "batched APSP min-plus relaxations/s (batch*n^3/time); % of VALU roofline"
 DEFAULT_WORKLOAD = "complete-8192-i32"
 
 # MI355X VALU peaks (256 CUs, 2.4 GHz).  A relaxation (one add, one min)
@@ -60,21 +67,23 @@ def phase3_relaxations_per_round(n: int, B: int) -> list[int]:
     return out
 
 
-def source_sha() -> str:
-    p = os.path.join(ROOT, "graph_all_pairs_amd", "csrc", "apsp.hip")
+def source_sha(name: str = "apsp.hip") -> str:
+    p = os.path.join(ROOT, "graph_all_pairs_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
 
 
-def read_traffic(workload: str, per_launch_relax: float):
-    """HBM bytes per Phase-3 launch from the committed rocprofv3 counter
-    summary, when it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"phase3_hbm_traffic_{workload}.md")
+def read_traffic(workload: str, per_launch_relax: float, kernel: str = "phase3",
+                 source: str = "apsp.hip"):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, when it was taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_hbm_traffic_{workload}.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
     m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", txt)
     m_b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", txt)
-    if not m_sha or not m_b or m_sha.group(1) != source_sha():
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(source):
         return None
     return float(m_b.group(1))
 
@@ -108,6 +117,136 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def cpu_baseline_batched(w, target_s: float):
+    """Time the oracle's per-graph Floyd-Warshall on the first graphs."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    batch, n = w.shape[0], w.shape[1]
+    f64 = w.dtype != np.int32
+
+    def run(k):
+        a = w[:k].astype(np.float64) if f64 else np.array(w[:k], copy=True)
+        t0 = time.perf_counter()
+        (orc.lib.oracle_fw_batched_f64 if f64 else orc.lib.oracle_fw_batched_i32)(
+            a.ctypes.data, k, n, a.shape[2], n * a.shape[2])
+        return time.perf_counter() - t0
+
+    probe = min(batch, 256)
+    per_graph = run(probe) / probe
+    k = int(max(1, min(batch, target_s / max(per_graph, 1e-12))))
+    dt = run(k)
+    return {
+        "value": k * n ** 3 / dt,
+        "unit": "relaxations/s",
+        "cores": orc.threads(),
+        "kind": "oracle",
+        "sample": f"plain Floyd-Warshall per graph (OpenMP over graphs) on the first {k} of "
+                  f"{batch} graphs of the same batch, n = {n} ({k * n ** 3:.3e} relaxations) "
+                  f"in {dt:.2f} s; rate = relaxations / time",
+    }
+
+
+def bench_batched(args) -> int:
+    """Many small graphs: one apsp_fw_batched_* launch per step."""
+    import numpy as np
+    import torch
+
+    import graph_all_pairs_amd as ga
+    import graphgen as gg
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = gg.BATCH_WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    w = gg.make_batch_workload(args.workload, ld=args.ld)
+    batch, n, ld = w.shape
+    sha = hashlib.sha256(np.ascontiguousarray(w).tobytes()).hexdigest()
+    log(f"workload {args.workload}: batch={batch} n={n} ld={ld} built in "
+        f"{time.perf_counter() - t0:.1f} s sha256={sha[:16]}")
+    is_int = w.dtype == np.int32
+    inf = gg.INF_I32 if is_int else float("inf")
+    fn = ga.apsp_fw_batched_i32 if is_int else ga.apsp_fw_batched_f32
+
+    pristine = torch.from_numpy(w).to(dev)
+    copies = [torch.empty_like(pristine) for _ in range(args.warmup + args.steps)]
+    for c in copies:
+        c.copy_(pristine)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(t):
+        st = fn(t.data_ptr(), batch, n, ld, n * ld, inf, sptr)
+        if st != ga.APSP_OK:
+            raise ga.APSPError(st, "apsp_fw_batched")
+
+    for i in range(args.warmup):
+        step(copies[i])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    # One kernel launch per step on torch's current stream: events recorded
+    # on that stream around each launch time the kernel itself.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(copies[args.warmup + i])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_per_step = 1e3 * wall / args.steps
+    relax = float(batch) * n ** 3
+    value = relax / (wall / args.steps)
+    arith = "int32" if is_int else "f32"
+    achieved = relax / (kern_ms * 1e-3)
+    peak = PEAK_RELAX[arith]
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms, kernel {kern_ms:.3f} ms/launch")
+    roofline = {
+        "bound": "alu",
+        "kernel": "fw_batched",
+        "achieved": achieved / 1e12,
+        "peak": peak / 1e12,
+        "unit": "Trelax/s",
+        "frac": achieved / peak,
+        "traffic": read_traffic(args.workload, relax, kernel="batched", source="batched.hip"),
+        "relax_per_launch": relax,
+        "avg_launch_ms": kern_ms,
+        "launches": args.steps,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline_batched(w, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.3e} relax/s on {cpu['cores']} threads")
+    rec = {
+        "metric": METRIC_BATCHED,
+        "value": value,
+        "unit": "relaxations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": arith,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch": batch, "n": n, "ld": ld,
+            "seed": spec["seed"], "matrix_dtype": arith, "input_sha256": sha,
+            "graphs_per_s": batch / (wall / args.steps),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +272,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.workload in gg.BATCH_WORKLOADS:
+        return bench_batched(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

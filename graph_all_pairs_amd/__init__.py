@@ -45,6 +45,7 @@ EXPORTS = (
     "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_set_int32_arith",
     "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
+    "apsp_fw_batched_i32", "apsp_fw_batched_f32",
 )
 
 _lib = None
@@ -88,6 +89,8 @@ def load(path: str | None = None):
         "apsp_fw_rounds_f32": ([vp, i64, i64, f32, i64, i64, vp], ctypes.c_int),
         "apsp_fw_timed_i32": ([vp, i64, i64, i32, vp, dp, lp, ip], ctypes.c_int),
         "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
+        "apsp_fw_batched_i32": ([vp, i64, i64, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_fw_batched_f32": ([vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
         "apsp_set_int32_arith": ([ctypes.c_int], ctypes.c_int),
         "apsp_get_int32_arith": ([], ctypes.c_int),
         "apsp_minplus_ceiling": ([ctypes.c_int, dp], ctypes.c_int),
@@ -121,6 +124,14 @@ def apsp_fw_rounds_i32(d_ptr, n, ld, inf, r0, r1, stream=0) -> int:
 
 def apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream=0) -> int:
     return load().apsp_fw_rounds_f32(d_ptr or None, n, ld, inf, r0, r1, stream or None)
+
+
+def apsp_fw_batched_i32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
+    return load().apsp_fw_batched_i32(d_ptr, batch, n, ld, stride, inf, stream)
+
+
+def apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
+    return load().apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream)
 
 
 def _timed(fn, d_ptr, n, ld, inf, stream):
@@ -245,3 +256,32 @@ def fw_timed(t, inf=None):
     if st != APSP_OK:
         raise APSPError(st, "apsp_fw_timed_" + kind)
     return ms, cnt, arith
+
+
+def fw_batched(t, inf=None):
+    """In-place APSP of every graph of a 3-D tensor t[g, :n, :n]
+    (n = t.shape[1] <= 128, rows contiguous) on the current stream."""
+    import torch
+    if t.dim() != 3:
+        raise ValueError("expected a 3-D tensor (batch, n, >= n columns)")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    batch, n = t.shape[0], t.shape[1]
+    if t.shape[2] < n:
+        raise ValueError("expected at least n columns")
+    if t.stride(2) != 1 and t.shape[2] > 1:
+        raise ValueError("tensor rows must be contiguous (stride(2) == 1)")
+    ld = t.stride(1) if n > 1 else max(t.shape[2], 1)
+    stride = t.stride(0) if batch > 1 else max((n - 1) * ld + n, 1)
+    if t.dtype == torch.int32:
+        fn, inf = apsp_fw_batched_i32, (INF_I32 if inf is None else int(inf))
+    elif t.dtype == torch.float32:
+        fn, inf = apsp_fw_batched_f32, (float("inf") if inf is None else float(inf))
+    else:
+        raise ValueError("dtype must be int32 or float32")
+    with torch.cuda.device(t.device):
+        st = fn(t.data_ptr(), batch, n, ld, stride, inf,
+                torch.cuda.current_stream(t.device).cuda_stream)
+    if st != APSP_OK:
+        raise APSPError(st, "apsp_fw_batched")
+    return t

@@ -45,8 +45,12 @@
 #include <type_traits>
 
 #include "apsp.h"
+#include "detail.h"
+#include "minplus.h"
 
 namespace {
+
+using namespace apsp_dev;
 
 constexpr int kB = 128;        // pivot block edge
 constexpr int kThreads = 256;  // Phase 2/3 workgroup size
@@ -64,101 +68,6 @@ constexpr int kWavesP3 = 3;    // waves per SIMD targeted by Phase 3 (<= 168 VGP
                                // with software-pipelined operand reads)
 constexpr int kWavesP2 = 4;    // waves per SIMD targeted by Phase 2 (<= 128 VGPRs)
 constexpr int kP3PerCu = 2;    // Phase-3 tiles per CU below which int32 calls stay in int32
-
-// ---------------------------------------------------------------------------
-// Element operations.  int32: wrap-free because every value is <= inf <=
-// 2^30 - 1.  float32: IEEE add and min (no NaN by precondition).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int32_t mp_min(int32_t a, int32_t b) { return min(a, b); }
-__device__ __forceinline__ float mp_min(float a, float b) {
-  float r;  // no NaN by precondition, so no canonicalising fminf
-  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-// min(a, b, c) as one v_min3.  Written as an instruction so that the compiler
-// keeps one three-input min per pair of candidates instead of re-balancing
-// the chain into two-input mins.
-__device__ __forceinline__ int32_t mp_min3(int32_t a, int32_t b, int32_t c) {
-  int32_t r;
-  asm("v_min3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float mp_min3(float a, float b, float c) {
-  float r;
-  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-template <typename T> struct Vec4;
-template <> struct Vec4<int32_t> { using type = int4; };
-template <> struct Vec4<float> { using type = float4; };
-
-template <typename T>
-__device__ __forceinline__ void load4(const T* __restrict__ p, T (&v)[4]) {
-  using V = typename Vec4<T>::type;
-  V x = *reinterpret_cast<const V*>(p);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(T* __restrict__ p, const T (&v)[4]) {
-  using V = typename Vec4<T>::type;
-  V x; x.x = v[0]; x.y = v[1]; x.z = v[2]; x.w = v[3];
-  *reinterpret_cast<V*>(p) = x;
-}
-
-// Four consecutive elements of row `row`, columns col .. col+3, of the
-// matrix; out-of-range elements read as inf.  VEC: one 128-bit load when the
-// whole quad is in range.  EDGE=false promises the quad is in range.
-template <typename T, bool VEC, bool EDGE>
-__device__ __forceinline__ void gload4(const T* __restrict__ d, int64_t ld, int64_t n,
-                                       int64_t row, int64_t col, T inf, T (&v)[4]) {
-  const T* p = d + row * ld + col;
-  if (!EDGE) {
-    if (VEC) { load4(p, v); }
-    else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = p[e];
-    }
-  } else {
-    if (row < n && col + 3 < n) {
-      if (VEC) { load4(p, v); }
-      else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = p[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (row < n && col + e < n) ? p[e] : inf;
-    }
-  }
-}
-
-template <typename T, bool VEC, bool EDGE>
-__device__ __forceinline__ void gstore4(T* __restrict__ d, int64_t ld, int64_t n,
-                                        int64_t row, int64_t col, const T (&v)[4]) {
-  T* p = d + row * ld + col;
-  if (!EDGE) {
-    if (VEC) { store4(p, v); }
-    else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = v[e];
-    }
-  } else {
-    if (row < n && col + 3 < n) {
-      if (VEC) { store4(p, v); }
-      else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = v[e];
-      }
-    } else if (row < n) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < n) p[e] = v[e];
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Min-plus tile update  C <- min(C, A (x) B)  for one workgroup.
@@ -359,108 +268,10 @@ constexpr int kLdsP2 = P2Row::kLdsElems > P2Col::kLdsElems ? P2Row::kLdsElems : 
 constexpr int kLdsP3 = P3::kLdsElems;
 constexpr int kLdsClose = 8 * kB;  // two pivot columns + two pivot rows, two buffers
 
-// ---------------------------------------------------------------------------
-// Phase 1 on a kB x kB block held in registers in the 8 x 8 micro-tile layout
-// of a 256-thread workgroup (the Phase-3 layout): Floyd-Warshall over the
-// block's own pivots t = 0 .. kB-1, in order, two pivots per step.
-//
-// With D the block before pivot t, the plain recurrence gives after pivots t
-// and t+1
-//   D1[x][y] = min(D[x][y], D[x][t] + D[t][y])
-//   D2[x][y] = min(D1[x][y], D1[x][t+1] + D1[t+1][y])
-//            = min(D[x][y], D[x][t] + D[t][y], D1[x][t+1] + D1[t+1][y]),
-// and the only D1 values that takes are column t+1 and row t+1:
-//   D1[x][t+1] = min(D[x][t+1], D[x][t] + D[t][t+1]),
-//   D1[t+1][y] = min(D[t+1][y], D[t+1][t] + D[t][y]).
-// So a step publishes columns t, t+1 and rows t, t+1 of D to LDS, every
-// thread forms D1's column and row entries for its own 8 rows and 8 columns,
-// and each element takes one three-input min.  Every stored value is the
-// same expression, evaluated the same way, as in the one-pivot-at-a-time
-// recurrence, so float results equal the plain sequential Floyd-Warshall on
-// the block bit for bit.  Ping-pong LDS buffers: one barrier per pivot pair.
-// ---------------------------------------------------------------------------
+// The kB x kB block of a 256-thread workgroup in the Phase-3 layout.
 template <typename T>
 __device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds) {
-  // lds: [2 buffers][4][kB] = column t, column t+1, row t, row t+1
-  const int tc = threadIdx.x % 16;
-  const int tr = threadIdx.x / 16;
-
-  // Pivot t = 64 g + 4 q + c lives in register slot s = 4 g + c of the
-  // threads with tc == q (its column) and tr == q (its row).
-  auto publish = [&](int buf, int owner, int slot) {
-    T* base = lds + buf * 4 * kB;
-    if (tc == owner) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        T v0[4] = {acc[0][slot + h], acc[1][slot + h], acc[2][slot + h], acc[3][slot + h]};
-        T v1[4] = {acc[4][slot + h], acc[5][slot + h], acc[6][slot + h], acc[7][slot + h]};
-        store4(&base[h * kB + tr * 4], v0);
-        store4(&base[h * kB + 64 + tr * 4], v1);
-      }
-    }
-    if (tr == owner) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        T v0[4] = {acc[slot + h][0], acc[slot + h][1], acc[slot + h][2], acc[slot + h][3]};
-        T v1[4] = {acc[slot + h][4], acc[slot + h][5], acc[slot + h][6], acc[slot + h][7]};
-        store4(&base[(2 + h) * kB + tc * 4], v0);
-        store4(&base[(2 + h) * kB + 64 + tc * 4], v1);
-      }
-    }
-  };
-
-  publish(0, 0, 0);
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-#pragma unroll 1
-    for (int q = 0; q < 16; ++q) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int t = 64 * g + 4 * q + 2 * cc;  // first pivot of the pair
-        const T* base = lds + cc * 4 * kB;      // pair index 32 g + 2 q + cc has parity cc
-        T a0[8], a1[8], b0[8], b1[8];
-        {
-          T v[4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            load4(&base[tr * 4 + 64 * h], v);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a0[4 * h + i] = v[i];
-            load4(&base[kB + tr * 4 + 64 * h], v);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a1[4 * h + i] = v[i];
-            load4(&base[2 * kB + tc * 4 + 64 * h], v);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b0[4 * h + j] = v[j];
-            load4(&base[3 * kB + tc * 4 + 64 * h], v);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b1[4 * h + j] = v[j];
-          }
-        }
-        const T d_t_t1 = base[2 * kB + t + 1];  // D[t][t+1]
-        const T d_t1_t = base[t + 1];           // D[t+1][t]
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a1[i] = mp_min(a1[i], a0[i] + d_t_t1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b1[j] = mp_min(b1[j], d_t1_t + b0[j]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = mp_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
-
-        // publish the next pair into the other buffer
-        if (cc == 0) {
-          publish(1, q, 4 * g + 2);
-        } else if (q < 15) {
-          publish(0, q + 1, 4 * g);
-        } else if (g == 0) {
-          publish(0, 0, 4);
-        }
-        __syncthreads();
-      }
-    }
-  }
+  close_block_t<T, kB, 8>(acc, lds);
 }
 
 // The same closure one pivot per step (d <- min(d, d[x][t] + d[t][y]), one
@@ -1121,6 +932,10 @@ int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms
 }
 
 }  // namespace
+
+// Library-internal host helpers for the other translation units.
+int apsp_detail_check_device() { return check_device(); }
+int apsp_detail_launch_status() { return launch_status(); }
 
 extern "C" {
 

@@ -1,0 +1,151 @@
+// Batched all-pairs shortest paths for many small graphs, one workgroup per
+// graph.
+//
+// The page "Loops into zones" (section "Many small graphs") parallelises a
+// graph algorithm over many independent small graphs by making each graph
+// one GPU block: the outer level runs graphs that never interact, the inner
+// level is one graph.  Here the inner level is Floyd-Warshall on a graph of
+// n <= 128 vertices, which is exactly one diagonal-block closure of the
+// blocked method (Phase 1 of the page "Katz and Kider", thesis section 4.6,
+// Algorithm 16): the graph's matrix is loaded into registers, closed two
+// pivots per barrier, and stored.
+//
+// Size classes (padded edge NB, micro-tile RT x RT, threads (NB/RT)^2):
+//   n <= 32:  NB = 32,  RT = 4,  64 threads (one wave per graph)
+//   n <= 64:  NB = 64,  RT = 8,  64 threads
+//   n <= 128: NB = 128, RT = 8,  256 threads
+// Rows and columns n .. NB-1 are isolated vertices: they load as inf and are
+// never stored, so the closure of the padded block restricted to [0, n) is
+// the closure of the graph.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "apsp.h"
+#include "detail.h"
+#include "minplus.h"
+
+namespace {
+
+using namespace apsp_dev;
+
+constexpr int64_t kMaxBatchedN = 128;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;  // workgroups; more graphs loop
+
+template <int NB, int RT>
+struct BatchShape {
+  static constexpr int kThr = NB / RT;          // threads per dimension
+  static constexpr int kThreads = kThr * kThr;
+  static constexpr int G = RT / 4;              // 4-wide groups per thread
+  static constexpr int S = NB / G;              // distance between groups
+};
+
+// VEC: 16-byte aligned quads (d, ld and stride all allow it); EDGE: n < NB.
+// The 8 x 8 micro-tile kernels are held to 168 VGPRs (3 waves per SIMD, a
+// few spills outside the pivot loop): measured 10 % faster than the 176
+// registers (2 waves) the compiler picks unconstrained, and faster than 4
+// waves (34-37 spills).
+template <typename T, int NB, int RT, bool VEC, bool EDGE>
+__global__ void __launch_bounds__((NB / RT) * (NB / RT))
+__attribute__((amdgpu_waves_per_eu(RT == 8 ? 3 : 1)))
+fw_batched(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf) {
+  using S = BatchShape<NB, RT>;
+  __shared__ __attribute__((aligned(16))) T lds[8 * NB];
+  const int tc = threadIdx.x % S::kThr;
+  const int tr = threadIdx.x / S::kThr;
+  for (int64_t g = blockIdx.x; g < batch; g += gridDim.x) {
+    T* m = d + g * stride;
+    T acc[RT][RT];
+#pragma unroll
+    for (int gi = 0; gi < S::G; ++gi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = gi * S::S + tr * 4 + i;
+#pragma unroll
+        for (int gj = 0; gj < S::G; ++gj) {
+          T v[4];
+          gload4<T, VEC, EDGE>(m, ld, n, row, gj * S::S + tc * 4, inf, v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[gi * 4 + i][gj * 4 + j] = v[j];
+        }
+      }
+    // The closure ends with a barrier after its last LDS reads, so the next
+    // graph may publish into the buffers right away.
+    close_block_t<T, NB, RT>(acc, lds);
+#pragma unroll
+    for (int gi = 0; gi < S::G; ++gi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = gi * S::S + tr * 4 + i;
+#pragma unroll
+        for (int gj = 0; gj < S::G; ++gj) {
+          T v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = acc[gi * 4 + i][gj * 4 + j];
+          gstore4<T, VEC, EDGE>(m, ld, n, row, gj * S::S + tc * 4, v);
+        }
+      }
+  }
+}
+
+template <typename T>
+bool inf_ok(T inf);
+template <>
+bool inf_ok<int32_t>(int32_t inf) { return inf >= 1 && inf <= 0x3FFFFFFF; }
+template <>
+bool inf_ok<float>(float inf) { return inf > 0.0f; }  // false for NaN
+
+template <typename T, int NB, int RT>
+void launch(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf, bool vec,
+            hipStream_t s) {
+  const dim3 grid((unsigned)(batch < kMaxGrid ? batch : kMaxGrid));
+  const dim3 block(BatchShape<NB, RT>::kThreads);
+  if (n == NB) {
+    if (vec) hipLaunchKernelGGL((fw_batched<T, NB, RT, true, false>), grid, block, 0, s, d, batch, n, ld, stride, inf);
+    else hipLaunchKernelGGL((fw_batched<T, NB, RT, false, false>), grid, block, 0, s, d, batch, n, ld, stride, inf);
+  } else {
+    if (vec) hipLaunchKernelGGL((fw_batched<T, NB, RT, true, true>), grid, block, 0, s, d, batch, n, ld, stride, inf);
+    else hipLaunchKernelGGL((fw_batched<T, NB, RT, false, true>), grid, block, 0, s, d, batch, n, ld, stride, inf);
+  }
+}
+
+template <typename T>
+int run_batched(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf,
+                void* stream) {
+  if (batch < 0 || n < 0 || n > kMaxBatchedN) return APSP_ERR_INVALID_VALUE;
+  if (batch == 0 || n == 0) return APSP_OK;
+  if (d == nullptr || ld < n) return APSP_ERR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(d) % sizeof(T)) != 0) return APSP_ERR_INVALID_VALUE;
+  // Graph g occupies elements [g*stride, g*stride + (n-1)*ld + n); graphs
+  // must not overlap and the last one must be addressable.
+  const int64_t span = (n - 1) * ld + n;
+  if (stride < span) return APSP_ERR_INVALID_VALUE;
+  if (batch > 1 && stride > (INT64_MAX / (int64_t)sizeof(T) - span) / (batch - 1))
+    return APSP_ERR_INVALID_VALUE;
+  if (!inf_ok<T>(inf)) return APSP_ERR_INVALID_VALUE;
+  int st = apsp_detail_check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool vec = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ld % 4 == 0 && stride % 4 == 0;
+  if (n <= 32) launch<T, 32, 4>(d, batch, n, ld, stride, inf, vec, s);
+  else if (n <= 64) launch<T, 64, 8>(d, batch, n, ld, stride, inf, vec, s);
+  else launch<T, 128, 8>(d, batch, n, ld, stride, inf, vec, s);
+  return apsp_detail_launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int apsp_fw_batched_i32(int32_t* d, int64_t batch, int64_t n, int64_t ld, int64_t stride,
+                        int32_t inf, void* stream) {
+  return run_batched<int32_t>(d, batch, n, ld, stride, inf, stream);
+}
+
+int apsp_fw_batched_f32(float* d, int64_t batch, int64_t n, int64_t ld, int64_t stride,
+                        float inf, void* stream) {
+  return run_batched<float>(d, batch, n, ld, stride, inf, stream);
+}
+
+}  // extern "C"

@@ -27,7 +27,10 @@ Graph families follow the workloads on the pages:
     Centrality Algorithms in GPU", experimental setup): beta undirected edges
     per new vertex, each stored as two directed edges with one shared weight;
   * small structured graphs (rings, paths, grids, disjoint rings) whose
-    shortest distances have closed forms.
+    shortest distances have closed forms;
+  * batches of many small independent graphs (the "many small graphs" case of
+    the page "Loops into zones"): graph g of a batch draws the same families
+    with counters offset by g * n * n, laid out as a (batch, n, ld) array.
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ __all__ = [
     "erdos_renyi", "complete", "complete_f32", "barabasi_albert",
     "ring", "undirected_path", "grid", "complete_equal", "edgeless",
     "two_rings", "WORKLOADS", "make_workload", "sha256_matrix", "pad_ld",
+    "erdos_renyi_batch", "complete_f32_batch", "BATCH_WORKLOADS", "make_batch_workload",
 ]
 
 INF_I32 = 0x3FFFFFFF          # the int32 "no edge" sentinel of the workloads
@@ -311,6 +315,59 @@ def two_rings(n1: int, n2: int, w=1, dtype=np.int32, inf=INF_I32,
     return m
 
 
+def _alloc_batch(batch: int, n: int, ld: int | None, dtype, inf, canary):
+    ld = n if ld is None else int(ld)
+    if ld < max(n, 1):
+        raise ValueError("ld must be >= max(n, 1)")
+    m = np.full((batch, n, ld), inf, dtype=dtype)
+    if ld > n:
+        m[:, :, n:] = canary
+    return m
+
+
+def _batch_chunks(batch: int, n: int, chunk_elems: int = 1 << 23):
+    step = max(1, chunk_elems // max(n * n, 1))
+    for g0 in range(0, batch, step):
+        yield g0, min(batch, g0 + step)
+
+
+def erdos_renyi_batch(batch: int, n: int, p: float, wlo: int, whi: int, seed: int,
+                      inf: int = INF_I32, ld: int | None = None,
+                      canary: int = -7) -> np.ndarray:
+    """``batch`` independent directed G(n, p) graphs with integer weights
+    uniform on [wlo, whi]; shape (batch, n, ld), int32."""
+    m = _alloc_batch(batch, n, ld, np.int32, inf, canary)
+    ij = np.arange(n * n, dtype=np.uint64).reshape(n, n)
+    for g0, g1 in _batch_chunks(batch, n):
+        g = np.arange(g0, g1, dtype=np.uint64)[:, None, None]
+        idx = g * np.uint64(n * n) + ij[None]
+        edge = _uniform01(u64_array(seed, _S_EDGE, idx)) < p
+        w = _uniform_int(u64_array(seed, _S_WEIGHT, idx), wlo, whi)
+        blk = np.where(edge, w, inf).astype(np.int32)
+        d = np.arange(n)
+        blk[:, d, d] = 0
+        m[g0:g1, :, :n] = blk
+    return m
+
+
+def complete_f32_batch(batch: int, n: int, seed: int, wlo: float = 0.01, whi: float = 1.0,
+                       ld: int | None = None, canary: float = -7.0,
+                       inf: float = float("inf")) -> np.ndarray:
+    """``batch`` independent complete digraphs with float32 weights as in
+    ``complete_f32``; shape (batch, n, ld)."""
+    m = _alloc_batch(batch, n, ld, np.float32, inf, canary)
+    ij = np.arange(n * n, dtype=np.uint64).reshape(n, n)
+    for g0, g1 in _batch_chunks(batch, n):
+        g = np.arange(g0, g1, dtype=np.uint64)[:, None, None]
+        idx = g * np.uint64(n * n) + ij[None]
+        u24 = (u64_array(seed, _S_WEIGHT, idx) >> np.uint64(40)).astype(np.float64)
+        blk = (wlo + (whi - wlo) * (u24 * (1.0 / 16777216.0))).astype(np.float32)
+        d = np.arange(n)
+        blk[:, d, d] = 0.0
+        m[g0:g1, :, :n] = blk
+    return m
+
+
 # ---- the named workloads --------------------------------------------------
 
 WORKLOADS = {
@@ -335,6 +392,28 @@ def make_workload(name: str, ld: int | None = None) -> np.ndarray:
         return barabasi_albert(w["n"], w["beta"], w["wlo"], w["whi"], w["seed"], ld=ld)
     if k == "complete_f32":
         return complete_f32(w["n"], w["seed"], ld=ld)
+    raise KeyError(name)
+
+
+# Batches of many small graphs: (batch, n, ld) arrays, one graph per
+# workgroup on the GPU.
+BATCH_WORKLOADS = {
+    "batch-er-8192x128-p0.1-i32": dict(kind="er", batch=8192, n=128, p=0.1, wlo=1, whi=100,
+                                       seed=11, dtype="i32"),
+    "batch-er-131072x32-p0.2-i32": dict(kind="er", batch=131072, n=32, p=0.2, wlo=1, whi=100,
+                                        seed=12, dtype="i32"),
+    "batch-complete-8192x100-f32": dict(kind="complete_f32", batch=8192, n=100, seed=13,
+                                        dtype="f32"),
+}
+
+
+def make_batch_workload(name: str, ld: int | None = None) -> np.ndarray:
+    """Build one of the named batch workloads, shape (batch, n, ld)."""
+    w = BATCH_WORKLOADS[name]
+    if w["kind"] == "er":
+        return erdos_renyi_batch(w["batch"], w["n"], w["p"], w["wlo"], w["whi"], w["seed"], ld=ld)
+    if w["kind"] == "complete_f32":
+        return complete_f32_batch(w["batch"], w["n"], w["seed"], ld=ld)
     raise KeyError(name)
 
 

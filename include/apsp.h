@@ -117,6 +117,35 @@ int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
                       double *phase_ms, int64_t *phase_launch, int *arith);
 
 /*
+ * Many small graphs at once: all-pairs shortest paths of `batch` independent
+ * graphs of n <= 128 vertices each, in place, one workgroup per graph.
+ * Defines: the page "Loops into zones", section "Many small graphs" (each
+ * graph is one GPU block, graphs never interact), with the per-graph work
+ * being the diagonal-block closure of the "Katz and Kider" page (thesis
+ * section 4.6, Phase 1 / Algorithm 16) on the whole graph.
+ *   d       device pointer; graph g's element (i, j) is d[g*stride + i*ld + j].
+ *           4-byte aligned; 128-bit access when d is 16-byte aligned and ld
+ *           and stride are multiples of 4.
+ *   batch   number of graphs, >= 0 (0 is a no-op).
+ *   n       vertices per graph, 0 <= n <= 128 (0 is a no-op).
+ *   ld      leading dimension of each graph, ld >= n.
+ *   stride  elements between consecutive graphs, stride >= (n-1)*ld + n (the
+ *           graphs must not overlap).
+ *   inf     sentinel, as for apsp_fw_i32 / apsp_fw_f32.
+ * Input preconditions and output as for apsp_fw_i32 / apsp_fw_f32, per graph.
+ * Arithmetic: int32 add and min (i32), IEEE binary32 add and min (f32); every
+ * graph is closed pivot by pivot in order, so float32 results equal the plain
+ * sequential Floyd-Warshall on that graph bit for bit.  Elements outside each
+ * graph's n x n block are never read or written.  Allocates nothing; work is
+ * enqueued on `stream`.  Errors: APSP_ERR_INVALID_VALUE for bad arguments
+ * (including n > 128) before any HIP call; otherwise as for apsp_fw_i32.
+ */
+int apsp_fw_batched_i32(int32_t *d, int64_t batch, int64_t n, int64_t ld, int64_t stride,
+                        int32_t inf, void *stream);
+int apsp_fw_batched_f32(float *d, int64_t batch, int64_t n, int64_t ld, int64_t stride,
+                        float inf, void *stream);
+
+/*
  * Arithmetic policy of int32 calls (process-wide; affects calls made after
  * it is set).  APSP_ARITH_AUTO (default): binary32 when it is exact (see
  * above) and Phase 3 has at least two 128 x 128 tiles per compute unit,

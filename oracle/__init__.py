@@ -46,6 +46,10 @@ def load(path: str = LIB):
     lib.oracle_fw_i32.restype = None
     lib.oracle_fw_f64.argtypes = [p, i64, i64, i64]
     lib.oracle_fw_f64.restype = None
+    lib.oracle_fw_batched_i32.argtypes = [p, i64, i64, i64, i64]
+    lib.oracle_fw_batched_i32.restype = None
+    lib.oracle_fw_batched_f64.argtypes = [p, i64, i64, i64, i64]
+    lib.oracle_fw_batched_f64.restype = None
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -87,6 +91,23 @@ class Oracle:
         n = a.shape[0]
         ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
         self.lib.oracle_fw_f64(a.ctypes.data, n, ld, n if k_end is None else int(k_end))
+        return a
+
+    def fw_batched_i32(self, m: np.ndarray) -> np.ndarray:
+        """Every graph of a (batch, n, ld) int32 array, closed independently."""
+        a = np.array(m, dtype=np.int32, order="C", copy=True)
+        b, n, ld = a.shape
+        if b and n:
+            self.lib.oracle_fw_batched_i32(a.ctypes.data, b, n, ld, n * ld)
+        return a
+
+    def fw_batched_f64(self, m: np.ndarray) -> np.ndarray:
+        """Every graph of a (batch, n, ld) array in binary64 (float32 inputs
+        are widened exactly)."""
+        a = np.array(m, dtype=np.float64, order="C", copy=True)
+        b, n, ld = a.shape
+        if b and n:
+            self.lib.oracle_fw_batched_f64(a.ctypes.data, b, n, ld, n * ld)
         return a
 
     def sssp_rows_i32(self, w: np.ndarray, inf: int, srcs) -> np.ndarray:

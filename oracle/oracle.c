@@ -65,7 +65,7 @@ int oracle_max_threads(void) {
 #endif
 }
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
 
 /* Floyd-Warshall on int32 distances, in place; pivots k = 0 .. k_end-1. */
 void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {
@@ -101,6 +101,25 @@ void oracle_fw_f64(double *d, int64_t n, int64_t ld, int64_t k_end) {
       }
     }
   }
+}
+
+/*
+ * Many independent graphs (the "many small graphs" case of the page "Loops
+ * into zones"): graph g is the n x n matrix at d + g * stride with leading
+ * dimension ld, closed by the same recurrence as above.  Graphs run in
+ * parallel (an inner parallel region, when nested, runs on its one thread,
+ * and the recurrence's results do not depend on its thread count).
+ */
+void oracle_fw_batched_i32(int32_t *d, int64_t batch, int64_t n, int64_t ld, int64_t stride) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nt)
+  for (int64_t g = 0; g < batch; ++g) oracle_fw_i32(d + g * stride, n, ld, n);
+}
+
+void oracle_fw_batched_f64(double *d, int64_t batch, int64_t n, int64_t ld, int64_t stride) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nt)
+  for (int64_t g = 0; g < batch; ++g) oracle_fw_f64(d + g * stride, n, ld, n);
 }
 
 /*

@@ -83,6 +83,34 @@ def test_round_range_errors(lib):
     assert ga.apsp_fw_rounds_f32(FAKE, 300, 300, 1.0, 0, 4) == ga.APSP_ERR_INVALID_VALUE
 
 
+@pytest.mark.parametrize("args", [
+    (FAKE, -1, 4, 4, 16, 100),         # batch < 0
+    (FAKE, 3, -1, 4, 16, 100),         # n < 0
+    (FAKE, 3, 129, 129, 129 * 129, 100),  # n > 128
+    (0, 3, 4, 4, 16, 100),             # null pointer
+    (FAKE, 3, 8, 7, 64, 100),          # ld < n
+    (FAKE, 3, 4, 4, 15, 100),          # stride < (n-1)*ld + n: graphs overlap
+    (FAKE, 3, 4, 8, 27, 100),          # same with padded rows
+    (FAKE + 2, 3, 4, 4, 16, 100),      # not 4-byte aligned
+    (FAKE, 3, 4, 4, 16, 0),            # bad inf
+    (FAKE, 3, 4, 4, 16, 0x40000000),
+    (FAKE, 1 << 40, 4, 4, 1 << 40, 100),  # last graph not addressable
+])
+def test_batched_argument_errors(lib, args):
+    assert ga.apsp_fw_batched_i32(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_batched_f32_bad_inf_and_no_ops(lib):
+    for inf in (0.0, -1.0, float("nan")):
+        assert ga.apsp_fw_batched_f32(FAKE, 3, 4, 4, 16, inf, 0) == ga.APSP_ERR_INVALID_VALUE
+    # empty batches and empty graphs touch nothing, whatever the pointer
+    assert ga.apsp_fw_batched_i32(0, 0, 4, 4, 16, 100, 0) == ga.APSP_OK
+    assert ga.apsp_fw_batched_i32(0, 5, 0, 1, 1, 100, 0) == ga.APSP_OK
+    assert ga.apsp_fw_batched_f32(0, 0, 128, 128, 128 * 128, 1.0, 0) == ga.APSP_OK
+    # the smallest legal stride: (n-1)*ld + n
+    assert ga.apsp_fw_batched_i32(0, 3, 4, 8, 28, 100, 0) == ga.APSP_ERR_INVALID_VALUE  # null
+
+
 def test_arith_policy_setter(lib):
     assert ga.apsp_get_int32_arith() == ga.APSP_ARITH_AUTO
     assert ga.apsp_set_int32_arith(7) == ga.APSP_ERR_INVALID_VALUE

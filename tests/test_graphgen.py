@@ -89,3 +89,26 @@ def test_workload_table_names():
 def test_zero_size():
     m = gg.erdos_renyi(0, 0.5, 1, 9, 1, ld=4)
     assert m.shape == (0, 4)
+
+
+def test_batch_generators():
+    b = gg.erdos_renyi_batch(6, 9, 0.3, 1, 50, 21, ld=12)
+    assert b.shape == (6, 9, 12) and b.dtype == np.int32
+    # graph 0 is the single-graph generator with the same seed; graph g uses
+    # the next n*n counters, so graphs differ
+    assert np.array_equal(b[0], gg.erdos_renyi(9, 0.3, 1, 50, 21, ld=12))
+    assert not np.array_equal(b[1], b[0])
+    assert np.all(b[:, :, 9:] == -7)
+    assert np.all(b[:, np.arange(9), np.arange(9)] == 0)
+    assert np.array_equal(b, gg.erdos_renyi_batch(6, 9, 0.3, 1, 50, 21, ld=12))
+    f = gg.complete_f32_batch(4, 5, 8)
+    assert f.shape == (4, 5, 5) and f.dtype == np.float32
+    assert np.array_equal(f[0], gg.complete_f32(5, 8))
+    off = ~np.eye(5, dtype=bool)
+    assert np.all((f[:, off] >= 0.01) & (f[:, off] < 1.0))
+
+
+def test_batch_workload_table():
+    for name, w in gg.BATCH_WORKLOADS.items():
+        assert name.startswith("batch-") and w["n"] <= 128 and w["batch"] >= 1
+        assert w["dtype"] in name

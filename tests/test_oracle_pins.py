@@ -219,3 +219,37 @@ def test_dijkstra_rows_match_fw_on_workload_shapes(orc):
         d = orc.fw_i32(w)
         src = np.arange(0, w.shape[0], 7)
         assert np.array_equal(orc.sssp_rows_i32(w, INF, src), d[src])
+
+
+# ---- many small graphs ------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_batched_oracle_is_the_definition_per_graph(orc, seed):
+    """Every graph of a batch, closed by the batched entry, equals the literal
+    minimum over simple paths of that graph (and nothing leaks between
+    graphs: each graph's answer depends on its own weights only)."""
+    rng = np.random.default_rng(9000 + seed)
+    n = int(rng.integers(1, 8))
+    batch = 25
+    ld = n + int(rng.integers(0, 3))
+    w = np.full((batch, n, ld), -7, dtype=np.int32)
+    for g in range(batch):
+        w[g, :, :n] = random_small_graph(rng, n, [0.2, 0.5, 0.8][g % 3], wmax=9, inf=INF)
+    got = orc.fw_batched_i32(w)
+    for g in range(batch):
+        assert np.array_equal(got[g, :, :n].astype(np.int64),
+                              brute_force_apsp(w[g, :, :n], INF).astype(np.int64))
+    assert np.all(got[:, :, n:] == -7)
+
+
+def test_batched_oracle_float_per_graph(orc):
+    rng = np.random.default_rng(77)
+    batch, n = 12, 6
+    w = np.stack([random_small_graph(rng, n, 0.6, wmax=4, inf=np.inf, floats=True)
+                  for _ in range(batch)])
+    got = orc.fw_batched_f64(w)
+    for g in range(batch):
+        want = brute_force_apsp(w[g], np.inf).astype(np.float64)
+        assert np.array_equal(np.isinf(got[g]), np.isinf(want))
+        fin = np.isfinite(want)
+        assert np.allclose(got[g][fin], want[fin], rtol=1e-12, atol=0)
