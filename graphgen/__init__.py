@@ -28,6 +28,9 @@ Graph families follow the workloads on the pages:
     per new vertex, each stored as two directed edges with one shared weight;
   * small structured graphs (rings, paths, grids, disjoint rings) whose
     shortest distances have closed forms;
+  * graphs with negative weights but no negative cycle (for Johnson's
+    algorithm): non-negative weights w0 shifted by vertex potentials,
+    w(u, v) = w0(u, v) + p(u) - p(v), so every cycle keeps its w0 length;
   * batches of many small independent graphs (the "many small graphs" case of
     the page "Loops into zones"): graph g of a batch draws the same families
     with counters offset by g * n * n, laid out as a (batch, n, ld) array.
@@ -44,6 +47,7 @@ __all__ = [
     "ring", "undirected_path", "grid", "complete_equal", "edgeless",
     "two_rings", "WORKLOADS", "make_workload", "sha256_matrix", "pad_ld",
     "erdos_renyi_batch", "complete_f32_batch", "BATCH_WORKLOADS", "make_batch_workload",
+    "erdos_renyi_potential", "csr_from_dense", "JOHNSON_WORKLOADS", "make_johnson_workload",
 ]
 
 INF_I32 = 0x3FFFFFFF          # the int32 "no edge" sentinel of the workloads
@@ -51,7 +55,7 @@ GAMMA = 0x9E3779B97F4A7C15    # SplitMix64 increment (odd, ~2^64 / phi)
 _M64 = (1 << 64) - 1
 
 # Streams: one independent counter space per purpose.
-_S_EDGE, _S_WEIGHT, _S_BA_PICK, _S_BA_WEIGHT = 1, 2, 3, 4
+_S_EDGE, _S_WEIGHT, _S_BA_PICK, _S_BA_WEIGHT, _S_POTENTIAL = 1, 2, 3, 4, 5
 
 
 def mix64(z: int) -> int:
@@ -368,6 +372,37 @@ def complete_f32_batch(batch: int, n: int, seed: int, wlo: float = 0.01, whi: fl
     return m
 
 
+def erdos_renyi_potential(n: int, p: float, wlo: int, whi: int, plo: int, phi: int,
+                          seed: int, inf: int = INF_I32, ld: int | None = None,
+                          canary: int = -7) -> np.ndarray:
+    """Directed G(n, p) whose weights may be negative but whose cycles are
+    not: w(u, v) = w0(u, v) + pot(u) - pot(v) with w0 uniform on [wlo, whi]
+    (wlo >= 0) and vertex potentials pot uniform on [plo, phi] (int32)."""
+    m = erdos_renyi(n, p, wlo, whi, seed, inf=inf, ld=ld, canary=canary)
+    pot = _uniform_int(u64_array(seed, _S_POTENTIAL, np.arange(n, dtype=np.uint64)), plo, phi)
+    blk = m[:, :n].astype(np.int64)
+    edge = (blk != inf) & ~np.eye(n, dtype=bool)
+    blk = np.where(edge, blk + pot[:, None] - pot[None, :], blk)
+    m[:, :n] = blk.astype(np.int32)
+    return m
+
+
+def csr_from_dense(m: np.ndarray, inf, n: int | None = None):
+    """Compressed sparse rows of the edges of a dense matrix: every (u, v)
+    with u != v and m[u, v] != inf.  Returns (row_ptr int64 [n+1],
+    col int32 [nnz], weight [nnz] in m's dtype), rows in order, columns
+    ascending within a row."""
+    n = m.shape[0] if n is None else n
+    blk = m[:n, :n]
+    mask = blk != inf
+    np.fill_diagonal(mask, False)
+    counts = mask.sum(axis=1)
+    row_ptr = np.zeros(n + 1, dtype=np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    rows, cols = np.nonzero(mask)
+    return row_ptr, cols.astype(np.int32), blk[rows, cols]
+
+
 # ---- the named workloads --------------------------------------------------
 
 WORKLOADS = {
@@ -405,6 +440,25 @@ BATCH_WORKLOADS = {
     "batch-complete-8192x100-f32": dict(kind="complete_f32", batch=8192, n=100, seed=13,
                                         dtype="f32"),
 }
+
+
+# Sparse graphs for Johnson's algorithm (CSR on the device, dense n x n
+# distances out).  The two sparse configurations of the dense workloads, and
+# a graph with negative weights.
+JOHNSON_WORKLOADS = {
+    "johnson-ba-16000-b8-i32": dict(dense="ba-16000-b8-i32"),
+    "johnson-er-2048-p0.05-i32": dict(dense="er-2048-p0.05-i32"),
+    "johnson-er-8192-p0.002-neg-i32": dict(kind="er_potential", n=8192, p=0.002, wlo=0,
+                                           whi=1000, plo=-500, phi=500, seed=21),
+}
+
+
+def make_johnson_workload(name: str) -> np.ndarray:
+    """Dense matrix of one of the Johnson workloads (row-major, ld = n)."""
+    w = JOHNSON_WORKLOADS[name]
+    if "dense" in w:
+        return make_workload(w["dense"])
+    return erdos_renyi_potential(w["n"], w["p"], w["wlo"], w["whi"], w["plo"], w["phi"], w["seed"])
 
 
 def make_batch_workload(name: str, ld: int | None = None) -> np.ndarray:

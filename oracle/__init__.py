@@ -50,6 +50,8 @@ def load(path: str = LIB):
     lib.oracle_fw_batched_i32.restype = None
     lib.oracle_fw_batched_f64.argtypes = [p, i64, i64, i64, i64]
     lib.oracle_fw_batched_f64.restype = None
+    lib.oracle_fw_guarded_i64.argtypes = [p, i64, i64, i64]
+    lib.oracle_fw_guarded_i64.restype = ctypes.c_int
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -109,6 +111,16 @@ class Oracle:
         if b and n:
             self.lib.oracle_fw_batched_f64(a.ctypes.data, b, n, ld, n * ld)
         return a
+
+    def fw_guarded(self, m: np.ndarray, inf: int):
+        """Shortest distances with negative weights allowed: returns
+        (distances as int64, has_negative_cycle).  Entries equal to inf are
+        "no edge"; candidates through inf are never formed."""
+        a = np.array(m, dtype=np.int64, order="C", copy=True)
+        n = a.shape[0]
+        ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
+        neg = self.lib.oracle_fw_guarded_i64(a.ctypes.data, n, ld, int(inf)) if n else 0
+        return a, bool(neg)
 
     def sssp_rows_i32(self, w: np.ndarray, inf: int, srcs) -> np.ndarray:
         a = np.ascontiguousarray(w, dtype=np.int32)

@@ -123,6 +123,36 @@ void oracle_fw_batched_f64(double *d, int64_t batch, int64_t n, int64_t ld, int6
 }
 
 /*
+ * Floyd-Warshall that also admits negative weights (the setting of Johnson's
+ * algorithm on the page "Johnson's APSP in Glushkov algorithmic algebras"):
+ * a candidate through k is formed only when both of its parts are finite,
+ * so the sentinel is never treated as a number.  int64 distances, in place
+ * on an int64 matrix.  Without a negative cycle the result is delta (a
+ * shortest walk is then a shortest simple path).  With one, some vertex on
+ * it ends with d(i, i) < 0; the function returns 1 in that case, else 0.
+ */
+int oracle_fw_guarded_i64(int64_t *d, int64_t n, int64_t ld, int64_t inf) {
+  int nt = oracle_max_threads();
+  for (int64_t k = 0; k < n; ++k) {
+    const int64_t *row_k = d + k * ld;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t i = 0; i < n; ++i) {
+      int64_t *row_i = d + i * ld;
+      int64_t d_ik = row_i[k];
+      if (d_ik == inf) continue;
+      for (int64_t j = 0; j < n; ++j) {
+        if (row_k[j] == inf) continue;
+        int64_t cand = d_ik + row_k[j];
+        if (cand < row_i[j]) row_i[j] = cand;
+      }
+    }
+  }
+  for (int64_t i = 0; i < n; ++i)
+    if (d[i * ld + i] < 0) return 1;
+  return 0;
+}
+
+/*
  * Dijkstra from `src` on the dense int32 weight matrix w (edge u->v exists
  * when u != v and w[u][v] != inf).  Writes delta(src, .) to out[0..n-1]:
  * unreachable vertices get exactly `inf`.  Returns 0, or -1 on bad arguments

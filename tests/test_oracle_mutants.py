@@ -43,6 +43,13 @@ MUTANTS = {
     "sssp_transposed_edge": ("const int32_t *wu = w + u * ld;\n    for (int64_t v = 0; v < n; ++v) { /* RelaxEdge(u, v) */\n      if (v == u || wu[v] == inf) continue;\n      int64_t cand = dist[u] + (int64_t)wu[v];",
                              "const int32_t *wu = w + u * ld;\n    for (int64_t v = 0; v < n; ++v) { /* RelaxEdge(u, v) */\n      if (v == u || w[v * ld + u] == inf) continue;\n      int64_t cand = dist[u] + (int64_t)w[v * ld + u];"),
     "sssp_dropped_dist_u": ("int64_t cand = dist[u] + (int64_t)wu[v];", "int64_t cand = (int64_t)wu[v];"),
+    # Floyd-Warshall with negative weights (INF-guarded), negative-cycle flag
+    "guard_dropped_ik": ("      if (d_ik == inf) continue;\n", ""),
+    "guard_dropped_kj": ("        if (row_k[j] == inf) continue;\n", ""),
+    "guard_cycle_le": ("if (d[i * ld + i] < 0) return 1;", "if (d[i * ld + i] <= 0) return 1;"),
+    "guard_cycle_never": ("if (d[i * ld + i] < 0) return 1;", "if (d[i * ld + i] < 0) return 0;"),
+    "guard_skips_last_pivot": ("int oracle_fw_guarded_i64(int64_t *d, int64_t n, int64_t ld, int64_t inf) {\n  int nt = oracle_max_threads();\n  for (int64_t k = 0; k < n; ++k) {",
+                               "int oracle_fw_guarded_i64(int64_t *d, int64_t n, int64_t ld, int64_t inf) {\n  int nt = oracle_max_threads();\n  for (int64_t k = 0; k < n - 1; ++k) {"),
 }
 
 
@@ -78,6 +85,27 @@ def _battery(o: oracle.Oracle) -> None:
     assert np.array_equal(o.sssp_rows_i32(w, INF, range(60)).astype(np.int64), ref)
 
 
+def _battery_guarded(o: oracle.Oracle) -> None:
+    w = np.array([[0, INF, INF], [INF, 0, -5], [INF, INF, 0]], dtype=np.int64)
+    got, neg = o.fw_guarded(w, INF)
+    assert not neg and got[0, 2] == INF and got[1, 2] == -5
+    assert o.fw_guarded(np.array([[0, 3], [-4, 0]], dtype=np.int64), INF)[1]
+    for seed in range(30):
+        rng = np.random.default_rng(300 + seed)
+        n = int(rng.integers(2, 8))
+        w0 = random_small_graph(rng, n, 0.5, 9, INF).astype(np.int64)
+        pot = rng.integers(-6, 7, size=n)
+        edge = (w0 != INF) & ~np.eye(n, dtype=bool)
+        w = np.where(edge, w0 + pot[:, None] - pot[None, :], w0)
+        got, neg = o.fw_guarded(w, INF)
+        assert not neg
+        assert np.array_equal(got, brute_force_apsp(w, INF).astype(np.int64))
+        u, v = 0, n - 1
+        w2 = w.copy()
+        w2[u, v], w2[v, u] = 3, -4   # cycle of weight -1
+        assert o.fw_guarded(w2, INF)[1]
+
+
 def _build_variant(tmp_path, name, edit):
     src = open(oracle.SRC).read()
     if edit is not None:
@@ -92,7 +120,9 @@ def _build_variant(tmp_path, name, edit):
 
 
 def test_battery_passes_on_unmodified_oracle(tmp_path):
-    _battery(_build_variant(tmp_path, "pristine", None))
+    o = _build_variant(tmp_path, "pristine", None)
+    _battery(o)
+    _battery_guarded(o)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -100,3 +130,4 @@ def test_battery_catches_mutant(tmp_path, name):
     o = _build_variant(tmp_path, name, MUTANTS[name])
     with pytest.raises(AssertionError):
         _battery(o)
+        _battery_guarded(o)

@@ -253,3 +253,66 @@ def test_batched_oracle_float_per_graph(orc):
         assert np.array_equal(np.isinf(got[g]), np.isinf(want))
         fin = np.isfinite(want)
         assert np.allclose(got[g][fin], want[fin], rtol=1e-12, atol=0)
+
+
+# ---- negative weights (Johnson's setting) -----------------------------------
+
+def _potential_graph(rng, n, p):
+    """Random graph with negative weights and no negative cycle: w0 >= 0
+    shifted by vertex potentials."""
+    w0 = random_small_graph(rng, n, p, wmax=9, inf=INF).astype(np.int64)
+    pot = rng.integers(-6, 7, size=n)
+    edge = (w0 != INF) & ~np.eye(n, dtype=bool)
+    return np.where(edge, w0 + pot[:, None] - pot[None, :], w0)
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_guarded_fw_negative_weights_brute_force(orc, seed):
+    rng = np.random.default_rng(20000 + seed)
+    n = int(rng.integers(1, 8))
+    w = _potential_graph(rng, n, [0.2, 0.5, 0.8][seed % 3])
+    got, neg = orc.fw_guarded(w, INF)
+    assert not neg
+    assert np.array_equal(got, brute_force_apsp(w, INF).astype(np.int64))
+
+
+def test_guarded_fw_matches_scipy_johnson_and_detects_cycles(orc):
+    sp = pytest.importorskip("scipy.sparse")
+    csg = pytest.importorskip("scipy.sparse.csgraph")
+    rng = np.random.default_rng(31)
+    for trial in range(30):
+        n = int(rng.integers(5, 40))
+        w = _potential_graph(rng, n, 0.15)
+        got, neg = orc.fw_guarded(w, INF)
+        assert not neg
+        mask = (w != INF) & ~np.eye(n, dtype=bool)
+        r, c = np.nonzero(mask)
+        # scipy treats explicit zeros as edges only when stored explicitly
+        g = sp.csr_matrix((w[r, c].astype(np.float64), (r, c)), shape=(n, n))
+        want = csg.johnson(g, directed=True)
+        want = np.where(np.isinf(want), INF, want).astype(np.int64)
+        assert np.array_equal(got, want)
+        # plant a negative cycle: u -> v -> u with total weight -1
+        u, v = rng.choice(n, size=2, replace=False)
+        w2 = w.copy()
+        w2[u, v], w2[v, u] = 3, -4
+        _, neg2 = orc.fw_guarded(w2, INF)
+        assert neg2
+        r2, c2 = np.nonzero((w2 != INF) & ~np.eye(n, dtype=bool))
+        g2 = sp.csr_matrix((w2[r2, c2].astype(np.float64), (r2, c2)), shape=(n, n))
+        with pytest.raises(csg.NegativeCycleError):
+            csg.johnson(g2, directed=True)
+
+
+def test_guarded_fw_never_uses_the_sentinel_as_a_number(orc):
+    # vertex 1 is unreachable from 0; its edge 1 -> 2 has weight -5, so an
+    # unguarded sum inf + (-5) would wrongly beat inf at (0, 2)
+    w = np.array([[0, INF, INF], [INF, 0, -5], [INF, INF, 0]], dtype=np.int64)
+    got, neg = orc.fw_guarded(w, INF)
+    assert not neg and got[0, 2] == INF and got[1, 2] == -5
+
+
+def test_guarded_fw_equals_plain_fw_without_negative_weights(orc):
+    w = gg.erdos_renyi(200, 0.03, 0, 50, 4)
+    got, neg = orc.fw_guarded(w, INF)
+    assert not neg and np.array_equal(got, orc.fw_i32(w).astype(np.int64))
