@@ -8,6 +8,13 @@ Functions mirror the C library:
     on a copy of the matrix (pivots 0 .. k_end-1), returned as a new array;
   * ``sssp_rows_i32(w, inf, srcs)`` / ``sssp_rows_f64(w, inf, srcs)``:
     Dijkstra from each listed source, one output row per source;
+  * ``fw_guarded(m, inf)``: Floyd-Warshall with negative weights allowed
+    (candidates through the sentinel are never formed) and a negative-cycle
+    flag;
+  * ``bf_rows_csr(row_ptr, col, w, n, srcs, inf)``: Bellman-Ford from each
+    listed source over a CSR graph (negative weights allowed);
+  * ``johnson_potentials(row_ptr, col, w, n)``: Johnson's h from an added
+    vertex with 0-weight edges to every vertex (Bellman-Ford);
   * ``apsp(m, inf)``: the full distance matrix of an int32 or float32 input
     (float32 is widened exactly to binary64 and the result stays binary64).
 """
@@ -52,6 +59,10 @@ def load(path: str = LIB):
     lib.oracle_fw_batched_f64.restype = None
     lib.oracle_fw_guarded_i64.argtypes = [p, i64, i64, i64]
     lib.oracle_fw_guarded_i64.restype = ctypes.c_int
+    lib.oracle_sssp_bf_csr_i64.argtypes = [p, p, p, i64, i64, p]
+    lib.oracle_sssp_bf_csr_i64.restype = ctypes.c_int
+    lib.oracle_sssp_bf_rows_i64.argtypes = [p, p, p, i64, p, i64, p, i64, p]
+    lib.oracle_sssp_bf_rows_i64.restype = ctypes.c_int
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -147,6 +158,38 @@ class Oracle:
             if rc != 0:
                 raise ValueError("oracle_sssp_rows_f64 rejected its arguments")
         return out[:, :n]
+
+    def bf_rows_csr(self, row_ptr, col, w, n: int, srcs, inf: int):
+        """Bellman-Ford from each listed source over a CSR graph (weights may
+        be negative).  Returns (rows as int64 with `inf` for unreached
+        vertices, per-source negative-cycle flags)."""
+        rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+        c = np.ascontiguousarray(col, dtype=np.int32)
+        wt = np.ascontiguousarray(w, dtype=np.int64)
+        s = np.ascontiguousarray(np.asarray(srcs, dtype=np.int64))
+        out = np.empty((len(s), max(n, 1)), dtype=np.int64)
+        neg = np.zeros(len(s), dtype=np.int32)
+        if len(s):
+            rc = self.lib.oracle_sssp_bf_rows_i64(rp.ctypes.data, c.ctypes.data, wt.ctypes.data,
+                                                  n, s.ctypes.data, len(s), out.ctypes.data,
+                                                  out.shape[1], neg.ctypes.data)
+            if rc != 0:
+                raise ValueError("oracle_sssp_bf_rows_i64 rejected its arguments")
+        out = out[:, :n]
+        out[out == np.iinfo(np.int64).max] = inf
+        return out, neg.astype(bool)
+
+    def johnson_potentials(self, row_ptr, col, w, n: int):
+        """The potentials h of Johnson's algorithm as the page builds them:
+        extendGraph adds vertex n with a 0-weight edge to every vertex, and
+        Bellman-Ford from it gives h(v), the shortest distance from the added
+        vertex.  Returns (h as int64 [n], has_negative_cycle)."""
+        rp = np.asarray(row_ptr, dtype=np.int64)
+        ext_rp = np.concatenate([rp, [rp[-1] + n]])
+        ext_col = np.concatenate([np.asarray(col, dtype=np.int32), np.arange(n, dtype=np.int32)])
+        ext_w = np.concatenate([np.asarray(w, dtype=np.int64), np.zeros(n, dtype=np.int64)])
+        rows, neg = self.bf_rows_csr(ext_rp, ext_col, ext_w, n + 1, [n], inf=0)
+        return rows[0, :n].copy(), bool(neg[0])
 
     def apsp(self, m: np.ndarray) -> np.ndarray:
         """Full distance matrix: int32 stays int32, float32 becomes float64."""

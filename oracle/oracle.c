@@ -241,3 +241,55 @@ int oracle_sssp_rows_f64(const double *w, int64_t n, int64_t ld, double inf,
     bad |= oracle_sssp_f64(w, n, ld, inf, srcs[s], out + s * ldo) != 0;
   return bad ? -1 : 0;
 }
+
+/*
+ * Bellman-Ford from `src` over a graph in compressed sparse rows (edge e of
+ * vertex u goes to col[e] with weight w[e], for e in [row_ptr[u],
+ * row_ptr[u+1])), following the Bellman-Ford operator of the page "Johnson's
+ * APSP in Glushkov algorithmic algebras": init (source 0, every other vertex
+ * unreached), rounds of RelaxEdges over every edge, then the negative-cycle
+ * condition cnc (some edge can still be relaxed).  A round that changes
+ * nothing leaves every later round unchanged too, so the rounds stop early
+ * there; after n rounds without that happening, an edge is still relaxable,
+ * which is the cnc condition.  Weights may be negative; sums are int64.
+ * Writes the shortest walk length from src to every vertex into dist
+ * (INT64_MAX when unreached).  Returns 1 when a negative cycle is reachable
+ * from src, 0 otherwise, -1 on bad arguments.
+ */
+int oracle_sssp_bf_csr_i64(const int64_t *row_ptr, const int32_t *col, const int64_t *w,
+                           int64_t n, int64_t src, int64_t *dist) {
+  if (n <= 0 || src < 0 || src >= n) return -1;
+  for (int64_t v = 0; v < n; ++v) dist[v] = INT64_MAX;
+  dist[src] = 0;
+  for (int64_t round = 0; round < n; ++round) {
+    int changed = 0;
+    for (int64_t u = 0; u < n; ++u) {
+      if (dist[u] == INT64_MAX) continue;
+      for (int64_t e = row_ptr[u]; e < row_ptr[u + 1]; ++e) {
+        const int64_t v = col[e];
+        const int64_t cand = dist[u] + w[e];
+        if (cand < dist[v]) { dist[v] = cand; changed = 1; }
+      }
+    }
+    if (!changed) return 0;
+  }
+  return 1;
+}
+
+/* Bellman-Ford from many sources (independent; OpenMP over sources).  Row s
+ * of out (leading dimension ldo) receives the distances from srcs[s];
+ * neg[s] the negative-cycle result.  Returns -1 if any call rejected its
+ * arguments, else 0. */
+int oracle_sssp_bf_rows_i64(const int64_t *row_ptr, const int32_t *col, const int64_t *w,
+                            int64_t n, const int64_t *srcs, int64_t nsrc, int64_t *out,
+                            int64_t ldo, int32_t *neg) {
+  int bad = 0;
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) reduction(| : bad)
+  for (int64_t s = 0; s < nsrc; ++s) {
+    const int r = oracle_sssp_bf_csr_i64(row_ptr, col, w, n, srcs[s], out + s * ldo);
+    if (r < 0) bad = 1;
+    else neg[s] = r;
+  }
+  return bad ? -1 : 0;
+}

@@ -50,6 +50,15 @@ MUTANTS = {
     "guard_cycle_never": ("if (d[i * ld + i] < 0) return 1;", "if (d[i * ld + i] < 0) return 0;"),
     "guard_skips_last_pivot": ("int oracle_fw_guarded_i64(int64_t *d, int64_t n, int64_t ld, int64_t inf) {\n  int nt = oracle_max_threads();\n  for (int64_t k = 0; k < n; ++k) {",
                                "int oracle_fw_guarded_i64(int64_t *d, int64_t n, int64_t ld, int64_t inf) {\n  int nt = oracle_max_threads();\n  for (int64_t k = 0; k < n - 1; ++k) {"),
+    # Bellman-Ford from one source (CSR), negative-cycle result
+    "bf_dropped_dist_u": ("const int64_t cand = dist[u] + w[e];", "const int64_t cand = w[e];"),
+    "bf_max_not_min": ("if (cand < dist[v]) { dist[v] = cand; changed = 1; }",
+                       "if (cand > dist[v] && dist[v] != INT64_MAX) { dist[v] = cand; changed = 1; }"),
+    "bf_one_round_short": ("for (int64_t round = 0; round < n; ++round) {",
+                           "for (int64_t round = 0; round < n - 1; ++round) {"),
+    "bf_cycle_never": ("    if (!changed) return 0;\n  }\n  return 1;",
+                       "    if (!changed) return 0;\n  }\n  return 0;"),
+    "bf_edge_target_is_source": ("const int64_t v = col[e];", "const int64_t v = u;"),
 }
 
 
@@ -106,6 +115,35 @@ def _battery_guarded(o: oracle.Oracle) -> None:
         assert o.fw_guarded(w2, INF)[1]
 
 
+def _battery_bellman_ford(o: oracle.Oracle) -> None:
+    # chain with negative weights: closed form
+    rp = np.array([0, 1, 2, 3, 3], dtype=np.int64)
+    col = np.array([1, 2, 3], dtype=np.int32)
+    wt = np.array([-1, -2, -3], dtype=np.int64)
+    h, neg = o.johnson_potentials(rp, col, wt, 4)
+    assert not neg and h.tolist() == [0, -1, -3, -6]
+    # two-vertex negative cycle
+    rp2, col2 = np.array([0, 1, 2], dtype=np.int64), np.array([1, 0], dtype=np.int32)
+    assert o.bf_rows_csr(rp2, col2, np.array([3, -4], dtype=np.int64), 2, [0], INF)[1][0]
+    # a ring whose shortest paths need n - 1 edges (the longest chain of rounds)
+    n = 9
+    rp3 = np.arange(n + 1, dtype=np.int64)
+    col3 = ((np.arange(n) + 1) % n).astype(np.int32)
+    got, neg = o.bf_rows_csr(rp3, col3, np.full(n, 2, dtype=np.int64), n, [0], INF)
+    assert not neg[0] and got[0].tolist() == [2 * j for j in range(n)]
+    for seed in range(30):
+        rng = np.random.default_rng(500 + seed)
+        n = int(rng.integers(2, 8))
+        w0 = random_small_graph(rng, n, 0.5, 9, INF).astype(np.int64)
+        pot = rng.integers(-6, 7, size=n)
+        edge = (w0 != INF) & ~np.eye(n, dtype=bool)
+        w = np.where(edge, w0 + pot[:, None] - pot[None, :], w0)
+        r, c, wv = gg.csr_from_dense(w, INF)
+        got, neg = o.bf_rows_csr(r, c, wv, n, range(n), INF)
+        assert not neg.any()
+        assert np.array_equal(got, brute_force_apsp(w, INF).astype(np.int64))
+
+
 def _build_variant(tmp_path, name, edit):
     src = open(oracle.SRC).read()
     if edit is not None:
@@ -123,6 +161,7 @@ def test_battery_passes_on_unmodified_oracle(tmp_path):
     o = _build_variant(tmp_path, "pristine", None)
     _battery(o)
     _battery_guarded(o)
+    _battery_bellman_ford(o)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -131,3 +170,4 @@ def test_battery_catches_mutant(tmp_path, name):
     with pytest.raises(AssertionError):
         _battery(o)
         _battery_guarded(o)
+        _battery_bellman_ford(o)

@@ -316,3 +316,94 @@ def test_guarded_fw_equals_plain_fw_without_negative_weights(orc):
     w = gg.erdos_renyi(200, 0.03, 0, 50, 4)
     got, neg = orc.fw_guarded(w, INF)
     assert not neg and np.array_equal(got, orc.fw_i32(w).astype(np.int64))
+
+
+# ---- Bellman-Ford from one source and Johnson's potentials ------------------
+
+def _csr(w):
+    return gg.csr_from_dense(w, INF)
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_bellman_ford_rows_brute_force(orc, seed):
+    rng = np.random.default_rng(40000 + seed)
+    n = int(rng.integers(1, 8))
+    w = _potential_graph(rng, n, [0.2, 0.5, 0.8][seed % 3])
+    rp, c, wt = _csr(w)
+    got, neg = orc.bf_rows_csr(rp, c, wt, n, range(n), INF)
+    assert not neg.any()
+    assert np.array_equal(got, brute_force_apsp(w, INF).astype(np.int64))
+
+
+def test_bellman_ford_matches_scipy_and_flags_reachable_cycles_only(orc):
+    sp = pytest.importorskip("scipy.sparse")
+    rng = np.random.default_rng(41)
+    for trial in range(20):
+        n = int(rng.integers(5, 60))
+        w = _potential_graph(rng, n, 0.1)
+        rp, c, wt = _csr(w)
+        got, neg = orc.bf_rows_csr(rp, c, wt, n, range(n), INF)
+        assert not neg.any()
+        r, cc = np.nonzero((w != INF) & ~np.eye(n, dtype=bool))
+        g = sp.csr_matrix((w[r, cc].astype(np.float64), (r, cc)), shape=(n, n))
+        want = csg.bellman_ford(g, directed=True)
+        assert np.array_equal(got, np.where(np.isinf(want), INF, want).astype(np.int64))
+    # vertices 0 -> 1 -> 2 -> 1 with cycle 1 <-> 2 of weight -1, vertex 3 alone
+    w = np.full((4, 4), INF, dtype=np.int64)
+    np.fill_diagonal(w, 0)
+    w[0, 1], w[1, 2], w[2, 1] = 5, 2, -3
+    rp, c, wt = _csr(w)
+    _, neg = orc.bf_rows_csr(rp, c, wt, 4, range(4), INF)
+    assert list(neg) == [True, True, True, False]
+
+
+def test_bellman_ford_self_loop_and_duplicate_edges(orc):
+    # CSR may hold self loops and parallel edges: a negative self loop is a
+    # negative cycle, a non-negative one changes nothing, the lighter of two
+    # parallel edges counts
+    rp = np.array([0, 3, 4, 4], dtype=np.int64)
+    col = np.array([1, 1, 0, 1], dtype=np.int32)
+    w = np.array([7, 4, 2, 0], dtype=np.int64)
+    got, neg = orc.bf_rows_csr(rp, col, w, 3, [0, 1, 2], INF)
+    assert not neg.any()
+    assert got.tolist() == [[0, 4, INF], [INF, 0, INF], [INF, INF, 0]]
+    w2 = w.copy()
+    w2[3] = -1
+    _, neg2 = orc.bf_rows_csr(rp, col, w2, 3, [0, 1, 2], INF)
+    assert list(neg2) == [True, True, False]
+
+
+def test_johnson_potentials_closed_form_chain(orc):
+    # 0 -> 1 -> 2 -> 3 with weights -1, -2, -3: h(v) is the prefix sum, and
+    # a vertex reached by nothing negative keeps h = 0
+    rp = np.array([0, 1, 2, 3, 3, 3], dtype=np.int64)
+    col = np.array([1, 2, 3], dtype=np.int32)
+    w = np.array([-1, -2, -3], dtype=np.int64)
+    h, neg = orc.johnson_potentials(rp, col, w, 5)
+    assert not neg and h.tolist() == [0, -1, -3, -6, 0]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_johnson_potentials_are_column_minima_and_reweight_non_negative(orc, seed):
+    # h(v) = distance from an added vertex joined to all by 0-weight edges =
+    # min over u of delta(u, v) (delta(v, v) = 0 gives h <= 0); with it every
+    # reweighted edge w + h(u) - h(v) is >= 0 (the page's property 2)
+    rng = np.random.default_rng(42000 + seed)
+    n = int(rng.integers(1, 8)) if seed < 30 else int(rng.integers(20, 80))
+    w = _potential_graph(rng, n, [0.2, 0.5, 0.8][seed % 3])
+    rp, c, wt = _csr(w)
+    h, neg = orc.johnson_potentials(rp, c, wt, n)
+    assert not neg
+    delta = brute_force_apsp(w, INF).astype(np.int64) if n <= 7 else orc.fw_guarded(w, INF)[0]
+    assert np.array_equal(h, delta.min(axis=0))
+    u = np.repeat(np.arange(n), np.diff(rp))
+    assert (wt + h[u] - h[c] >= 0).all()
+
+
+def test_johnson_potentials_flag_any_negative_cycle(orc):
+    # the added vertex reaches every vertex, so every negative cycle counts
+    w = np.full((5, 5), INF, dtype=np.int64)
+    np.fill_diagonal(w, 0)
+    w[3, 4], w[4, 3] = 1, -2
+    rp, c, wt = _csr(w)
+    assert orc.johnson_potentials(rp, c, wt, 5)[1]
