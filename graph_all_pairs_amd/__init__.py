@@ -13,6 +13,9 @@ streams are integers):
     apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream) -> status
     apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
     apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
+    apsp_fw_batched_i32 / _f32(d_ptr, batch, n, ld, stride, inf, stream) -> status
+    apsp_johnson_i32(row_ptr, col, w, n, nnz, d_ptr, ld, inf, h_ptr, delta, stream) -> status
+    apsp_johnson_timed_i32(...same...) -> (status, ms[4], counts[4])
     apsp_set_int32_arith(mode), apsp_get_int32_arith(), apsp_minplus_ceiling(arith)
     apsp_pivot_block(n), apsp_status_string(s), apsp_last_hip_error(), apsp_version()
 
@@ -20,6 +23,10 @@ Tensor convenience:
     fw(t, inf=None)              in-place APSP of a 2-D int32/float32 CUDA tensor
     fw_rounds(t, r0, r1, inf=None)
     fw_timed(t, inf=None)        -> (phase_ms, launches, arith), synchronised
+    fw_batched(t, inf=None)      in-place APSP of every graph of a 3-D tensor
+    johnson(row_ptr, col, w, out=None, inf=None, h=None, delta=-1)
+                                 Johnson's APSP of a CSR graph into a dense
+                                 (n, >= n) int32 tensor, synchronised
 """
 from __future__ import annotations
 
@@ -32,6 +39,8 @@ APSP_OK = 0
 APSP_ERR_INVALID_VALUE = 1
 APSP_ERR_NO_DEVICE = 2
 APSP_ERR_LAUNCH = 3
+APSP_ERR_NEGATIVE_CYCLE = 4
+APSP_ERR_RANGE = 5
 
 APSP_ARITH_AUTO = 0
 APSP_ARITH_F32_WHEN_EXACT = 1
@@ -45,7 +54,8 @@ EXPORTS = (
     "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_set_int32_arith",
     "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
-    "apsp_fw_batched_i32", "apsp_fw_batched_f32",
+    "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
+    "apsp_johnson_timed_i32",
 )
 
 _lib = None
@@ -58,6 +68,16 @@ class APSPError(RuntimeError):
         if status == APSP_ERR_LAUNCH:
             msg += f" (hipError {apsp_last_hip_error()})"
         super().__init__(msg)
+
+
+class NegativeCycleError(APSPError):
+    """The graph has a cycle of negative total weight."""
+
+
+def _raise(status: int, what: str):
+    if status == APSP_ERR_NEGATIVE_CYCLE:
+        raise NegativeCycleError(status, what)
+    raise APSPError(status, what)
 
 
 def lib_path() -> str:
@@ -91,6 +111,9 @@ def load(path: str | None = None):
         "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
         "apsp_fw_batched_i32": ([vp, i64, i64, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_batched_f32": ([vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_johnson_i32": ([vp, vp, vp, i64, i64, vp, i64, i32, vp, i32, vp], ctypes.c_int),
+        "apsp_johnson_timed_i32": ([vp, vp, vp, i64, i64, vp, i64, i32, vp, i32, vp, dp, lp],
+                                   ctypes.c_int),
         "apsp_set_int32_arith": ([ctypes.c_int], ctypes.c_int),
         "apsp_get_int32_arith": ([], ctypes.c_int),
         "apsp_minplus_ceiling": ([ctypes.c_int, dp], ctypes.c_int),
@@ -132,6 +155,23 @@ def apsp_fw_batched_i32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
 
 def apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
     return load().apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream)
+
+
+def apsp_johnson_i32(row_ptr, col, w, n, nnz, d_ptr, ld, inf, h_ptr=0, delta=-1, stream=0) -> int:
+    return load().apsp_johnson_i32(row_ptr or None, col or None, w or None, n, nnz, d_ptr or None,
+                                   ld, inf, h_ptr or None, delta, stream or None)
+
+
+def apsp_johnson_timed_i32(row_ptr, col, w, n, nnz, d_ptr, ld, inf, h_ptr=0, delta=-1, stream=0):
+    """(status, phase ms [validate, Bellman-Ford, reweight, searches],
+    counts [Bellman-Ford rounds, search steps, vertices removed, edge
+    relaxations])."""
+    ms = (ctypes.c_double * 4)()
+    counts = (ctypes.c_int64 * 4)()
+    st = load().apsp_johnson_timed_i32(row_ptr or None, col or None, w or None, n, nnz,
+                                       d_ptr or None, ld, inf, h_ptr or None, delta,
+                                       stream or None, ms, counts)
+    return st, list(ms), list(counts)
 
 
 def _timed(fn, d_ptr, n, ld, inf, stream):
@@ -285,3 +325,42 @@ def fw_batched(t, inf=None):
     if st != APSP_OK:
         raise APSPError(st, "apsp_fw_batched")
     return t
+
+
+def johnson(row_ptr, col, w, out=None, inf=None, h=None, delta=-1, timed=False):
+    """Johnson's APSP of a CSR graph (device tensors: row_ptr int64 [n+1],
+    col int32 [nnz], w int32 [nnz]) into out[:n, :n] (int32, rows contiguous;
+    allocated as (n, n) when None).  h: optional int32 [n] output of the
+    potentials.  Synchronous.  Returns out, or (out, phase_ms, counts) with
+    timed=True (see apsp_johnson_timed_i32).  Raises NegativeCycleError on a negative cycle."""
+    import torch
+    for name, t, dt in (("row_ptr", row_ptr, torch.int64), ("col", col, torch.int32),
+                        ("w", w, torch.int32)):
+        if not t.is_cuda or t.dtype != dt or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D {dt} CUDA tensor")
+    n = row_ptr.shape[0] - 1
+    nnz = col.shape[0]
+    if n < 0 or w.shape[0] != nnz:
+        raise ValueError("row_ptr needs n + 1 entries and w one weight per column index")
+    if out is None:
+        out = torch.empty((n, n), dtype=torch.int32, device=row_ptr.device)
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape[0] != n or out.shape[1] < n:
+        raise ValueError("out must be an int32 (n, >= n) tensor")
+    if n > 1 and out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    ld = out.stride(0) if n > 1 else max(out.shape[1], 1)
+    if h is not None and (h.dtype != torch.int32 or h.numel() != n or not h.is_contiguous()):
+        raise ValueError("h must be a contiguous int32 tensor of n entries")
+    inf = INF_I32 if inf is None else int(inf)
+    hp = h.data_ptr() if h is not None else 0
+    with torch.cuda.device(row_ptr.device):
+        s = torch.cuda.current_stream(row_ptr.device).cuda_stream
+        args = (row_ptr.data_ptr(), col.data_ptr() if nnz else 0, w.data_ptr() if nnz else 0,
+                n, nnz, out.data_ptr() if n else 0, ld, inf, hp, int(delta), s)
+        if timed:
+            st, ms, counts = apsp_johnson_timed_i32(*args)
+        else:
+            st, ms, counts = apsp_johnson_i32(*args), None, None
+    if st != APSP_OK:
+        _raise(st, "apsp_johnson_i32")
+    return (out, ms, counts) if timed else out

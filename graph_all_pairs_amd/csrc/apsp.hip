@@ -989,6 +989,8 @@ const char* apsp_status_string(int status) {
     case APSP_ERR_INVALID_VALUE: return "APSP_ERR_INVALID_VALUE: invalid argument";
     case APSP_ERR_NO_DEVICE: return "APSP_ERR_NO_DEVICE: current device is not gfx950";
     case APSP_ERR_LAUNCH: return "APSP_ERR_LAUNCH: kernel launch failed";
+    case APSP_ERR_NEGATIVE_CYCLE: return "APSP_ERR_NEGATIVE_CYCLE: the graph has a negative cycle";
+    case APSP_ERR_RANGE: return "APSP_ERR_RANGE: a value is outside the representable range";
     default: return "APSP: unknown status";
   }
 }

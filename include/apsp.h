@@ -7,7 +7,10 @@
  * 4.6 and its Algorithms 16-18): the matrix is cut into square pivot blocks;
  * round K closes the diagonal block (K,K) (Phase 1), then updates the blocks
  * in pivot row K and pivot column K (Phase 2), then every remaining block
- * (Phase 3), and the pivot moves one block down the diagonal.
+ * (Phase 3), and the pivot moves one block down the diagonal.  Next to it:
+ * many small graphs at once (apsp_fw_batched_*) and Johnson's algorithm for
+ * sparse graphs with negative weights (apsp_johnson_*), whose own contracts
+ * are stated at their declarations.
  *
  * Only plain C types cross this boundary.  `stream` is a hipStream_t passed
  * as an opaque pointer (NULL = the null stream).
@@ -64,7 +67,9 @@ enum {
   APSP_OK = 0,
   APSP_ERR_INVALID_VALUE = 1,
   APSP_ERR_NO_DEVICE = 2,
-  APSP_ERR_LAUNCH = 3
+  APSP_ERR_LAUNCH = 3,
+  APSP_ERR_NEGATIVE_CYCLE = 4,  /* the graph has a cycle of negative weight */
+  APSP_ERR_RANGE = 5            /* a value the call must represent is out of range */
 };
 
 /*
@@ -144,6 +149,75 @@ int apsp_fw_batched_i32(int32_t *d, int64_t batch, int64_t n, int64_t ld, int64_
                         int32_t inf, void *stream);
 int apsp_fw_batched_f32(float *d, int64_t batch, int64_t n, int64_t ld, int64_t stride,
                         float inf, void *stream);
+
+/*
+ * Johnson's all-pairs shortest paths of a sparse digraph whose edge weights
+ * may be negative, written as a dense distance matrix.
+ * Defines: the page "Johnson's APSP in Glushkov algorithmic algebras" (CEUR
+ * Vol-1631): extendGraph (an added vertex q with 0-weight edges to every
+ * vertex), BellmanFord from q with the negative-cycle condition cnc, giving
+ * the potentials h; UpdateWeights w'(u,v) = w(u,v) + h(u) - h(v) >= 0; a
+ * single-source search D(i) from every vertex on w'; and to(D, i), d(i,j) =
+ * D'(j) - h(i) + h(j).  The single-source searches follow the delta-stepping
+ * scheme of the page "Delta-stepping SSSP on CPU and GPU" (CEUR Vol-1662,
+ * Algorithm 1) with the threshold rule of the Johnson page's parallel
+ * ExtractMin.
+ *   row_ptr  device, n + 1 int64 offsets: the out-edges of vertex u are
+ *            e in [row_ptr[u], row_ptr[u+1]); row_ptr[0] = 0, non-decreasing,
+ *            row_ptr[n] = nnz.  8-byte aligned.
+ *   col, w   device, nnz int32 each: edge e goes to col[e] (0 <= col[e] < n)
+ *            with weight w[e], -inf < w[e] < inf.  Self loops and parallel
+ *            edges are allowed (the lightest parallel edge counts; a
+ *            negative self loop is a negative cycle).  May be NULL when
+ *            nnz = 0.
+ *   n, nnz   vertices (0 <= n < 2^31 - 1; n = 0 is a no-op) and edges
+ *            (0 <= nnz < 2^31).
+ *   d, ld    device output, element (i, j) at d[i*ld + j], ld >= n, 4-byte
+ *            aligned; only the leading n x n block is written.  Must not
+ *            overlap the graph arrays or h.
+ *   inf      the "no path" sentinel written for unreachable pairs,
+ *            1 <= inf <= 0x3FFFFFFF.
+ *   h        optional device output (NULL or n int32): the potentials h(v),
+ *            the shortest distance from the added vertex q (always <= 0;
+ *            all zero when no weight is negative).
+ *   delta    bucket width of the searches (>= 0), or < 0 for automatic (the
+ *            mean reweighted edge weight).  0 takes one distance value per
+ *            step, like Dijkstra.  The result does not depend on delta.
+ * Output: d[i][j] = the shortest-path distance from i to j (exact), d[i][i]
+ * = 0, and exactly inf where j is unreachable from i.
+ * Preconditions checked on the device before anything is written: the CSR
+ * structure and the weight range above (else APSP_ERR_INVALID_VALUE).
+ * Results must be representable: every finite distance lies strictly between
+ * -inf and inf (else APSP_ERR_RANGE; d is then partly written).
+ * Negative cycle: returns APSP_ERR_NEGATIVE_CYCLE and leaves d untouched (h,
+ * when given, is left untouched too).
+ * Synchronous: the call reads device results between its steps and returns
+ * after all of its work on `stream` has completed.  It takes stream-ordered
+ * scratch (hipMallocAsync on `stream`) of about 14n + 8nnz bytes and frees
+ * it before returning.  The row of each source lives in one workgroup's
+ * LDS (4n bytes plus a small queue), which bounds n to about 38 000 on
+ * gfx950; a larger n returns APSP_ERR_RANGE before any work.
+ * Other errors as for apsp_fw_i32.
+ */
+int apsp_johnson_i32(const int64_t *row_ptr, const int32_t *col, const int32_t *w,
+                     int64_t n, int64_t nnz, int32_t *d, int64_t ld, int32_t inf,
+                     int32_t *h, int32_t delta, void *stream);
+
+/*
+ * Measurement variant of apsp_johnson_i32: the same work, with HIP events on
+ * `stream` around each step.  phase_ms (4 doubles, may be NULL) receives the
+ * event time of: 0 = validation, 1 = Bellman-Ford (including its host
+ * checks; no rounds run when no weight is negative) and the int32
+ * potentials, 2 = reweighting, 3 = the
+ * single-source searches with the write-out.  counts (4 int64, may be
+ * NULL) receives: 0 = Bellman-Ford rounds launched, 1 = search steps, 2 =
+ * vertices removed from the marks, 3 = edge relaxations (1-3 summed over
+ * all sources; every source relaxes each edge it reaches at least once).
+ */
+int apsp_johnson_timed_i32(const int64_t *row_ptr, const int32_t *col, const int32_t *w,
+                           int64_t n, int64_t nnz, int32_t *d, int64_t ld, int32_t inf,
+                           int32_t *h, int32_t delta, void *stream, double *phase_ms,
+                           int64_t *counts);
 
 /*
  * Arithmetic policy of int32 calls (process-wide; affects calls made after

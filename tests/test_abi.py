@@ -142,3 +142,35 @@ def test_single_hip_runtime_in_process(lib):
     maps = open("/proc/self/maps").read().splitlines()
     paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(paths) == 1, paths
+
+
+@pytest.mark.parametrize("args", [
+    # row_ptr, col, w, n, nnz, d, ld, inf
+    (FAKE, FAKE, FAKE, -1, 4, FAKE, 4, 100),          # n < 0
+    (FAKE, FAKE, FAKE, 4, -1, FAKE, 4, 100),          # nnz < 0
+    (0, FAKE, FAKE, 4, 4, FAKE, 4, 100),              # null row_ptr
+    (FAKE, 0, FAKE, 4, 4, FAKE, 4, 100),              # null col with edges
+    (FAKE, FAKE, 0, 4, 4, FAKE, 4, 100),              # null weights with edges
+    (FAKE, FAKE, FAKE, 4, 4, 0, 4, 100),              # null output
+    (FAKE, FAKE, FAKE, 8, 4, FAKE, 7, 100),           # ld < n
+    (FAKE + 4, FAKE, FAKE, 4, 4, FAKE, 4, 100),       # row_ptr not 8-byte aligned
+    (FAKE, FAKE + 2, FAKE, 4, 4, FAKE, 4, 100),       # col not 4-byte aligned
+    (FAKE, FAKE, FAKE, 4, 4, FAKE + 1, 4, 100),       # d not 4-byte aligned
+    (FAKE, FAKE, FAKE, 4, 4, FAKE, 4, 0),             # inf < 1
+    (FAKE, FAKE, FAKE, 4, 4, FAKE, 4, 0x40000000),    # inf too large
+    (FAKE, FAKE, FAKE, 1 << 31, 4, FAKE, 1 << 31, 100),  # n too large
+    (FAKE, FAKE, FAKE, 4, 1 << 31, FAKE, 4, 100),     # nnz too large
+])
+def test_johnson_argument_errors(lib, args):
+    assert ga.apsp_johnson_i32(*args, 0, -1, 0) == ga.APSP_ERR_INVALID_VALUE
+    st, ms, counts = ga.apsp_johnson_timed_i32(*args, 0, -1, 0)
+    assert st == ga.APSP_ERR_INVALID_VALUE and counts == [0, 0, 0, 0]
+
+
+def test_johnson_empty_graph_is_a_no_op(lib):
+    assert ga.apsp_johnson_i32(0, 0, 0, 0, 0, 0, 1, 100, 0, -1, 0) == ga.APSP_OK
+
+
+def test_status_strings_for_negative_weights(lib):
+    assert "NEGATIVE_CYCLE" in ga.apsp_status_string(ga.APSP_ERR_NEGATIVE_CYCLE)
+    assert "RANGE" in ga.apsp_status_string(ga.APSP_ERR_RANGE)
