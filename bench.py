@@ -9,8 +9,9 @@ Prints ONE JSON line:
   value        relaxations/s = n^3 / (wall time per step), n = logical size
   roofline     the Phase-3 kernel (the hot loop): algorithmic relaxations per
                launch / its average launch duration (HIP events recorded on
-               the kernel's stream around every launch, inside the timed
-               region), against the int32 VALU min-plus peak
+               the kernel's stream around every launch of the last two calls
+               of the timed region), against the VALU min-plus peak of the
+               arithmetic the call used
   cpu_baseline the CPU oracle (plain Floyd-Warshall) timed on this host on a
                bounded sample of the same workload: its first k pivots
 
@@ -24,7 +25,7 @@ With --workload johnson-... (sparse graphs, see graphgen.JOHNSON_WORKLOADS) a
 step is one apsp_johnson_timed_i32 call (CSR on the device, dense n x n
 distances out); value = n^3 / (wall time per step), the rate a dense
 Floyd-Warshall would need to match it, and the same matrix is also timed
-through apsp_fw_i32 when its weights are non-negative.
+through apsp_fw_i32 (apsp_fw_signed_i32 when some weight is negative).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -335,24 +336,24 @@ def bench_johnson(args) -> int:
         f"bellman-ford, reweight, search] {[round(x, 3) for x in per]}; counts per call "
         f"[bf rounds, steps, removed, relaxations] {cnt}")
 
-    fw_ms = None
-    if not neg:
-        d = torch.from_numpy(w).to(dev)
-        ref = torch.empty_like(d)
-        times = []
-        for _ in range(2):
-            ref.copy_(d)
-            torch.cuda.synchronize()
-            t1 = time.perf_counter()
-            ga.fw(ref, gg.INF_I32)
-            torch.cuda.synchronize()
-            times.append(time.perf_counter() - t1)
-        fw_ms = 1e3 * min(times)
-        same = bool(torch.equal(ref, out))
-        log(f"blocked Floyd-Warshall on the same matrix: {fw_ms:.2f} ms, results equal: {same}")
-        if not same:
-            raise RuntimeError("Johnson and Floyd-Warshall disagree")
-        del d, ref
+    # The blocked Floyd-Warshall on the same dense matrix (its negative-weight
+    # entry when some weight is negative), for comparison.
+    d = torch.from_numpy(w).to(dev)
+    ref = torch.empty_like(d)
+    times = []
+    for _ in range(2):
+        ref.copy_(d)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        (ga.fw_signed if neg else ga.fw)(ref, gg.INF_I32)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t1)
+    fw_ms = 1e3 * min(times)
+    same = bool(torch.equal(ref, out))
+    log(f"blocked Floyd-Warshall on the same matrix: {fw_ms:.2f} ms, results equal: {same}")
+    if not same:
+        raise RuntimeError("Johnson and Floyd-Warshall disagree")
+    del d, ref
 
     # The search kernel: algorithmic HBM bytes per launch are the n x n
     # result written once plus the graph read once (packed edges, offsets).
@@ -399,7 +400,8 @@ def bench_johnson(args) -> int:
         "config": {
             "workload": args.workload, "n": n, "nnz": nnz, "negative_weights": neg,
             "input_sha256": sha, "fw_ms_per_call": fw_ms,
-            "speedup_vs_fw": (fw_ms / ms_per_step) if fw_ms else None,
+            "fw_entry": "apsp_fw_signed_i32" if neg else "apsp_fw_i32",
+            "speedup_vs_fw": fw_ms / ms_per_step,
         },
         "ms_per_step_by_phase": dict(zip(["validate", "bellman_ford", "reweight", "search"], per)),
         "counts_per_step": dict(zip(["bellman_ford_rounds", "search_steps", "removed",
@@ -462,44 +464,65 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    fn = ga.apsp_fw_timed_i32 if is_int else ga.apsp_fw_timed_f32
 
-    def step(t):
-        st, ms, cnt, arith = fn(t.data_ptr(), n, ld, inf, sptr)
-        if st != ga.APSP_OK:
-            raise ga.APSPError(st, "apsp_fw_timed")
-        return ms, cnt, arith
+    timed_fn = ga.apsp_fw_timed_i32 if is_int else ga.apsp_fw_timed_f32
+    plain_fn = ga.apsp_fw_i32 if is_int else ga.apsp_fw_f32
 
+    # The arithmetic an int32 call takes depends only on the matrix: learn it
+    # from one synchronised timed call during the warm-up.
+    arith_code = None
     for i in range(args.warmup):
-        step(copies[i])
+        if i == 0:
+            st, _, _, arith_code = timed_fn(copies[i].data_ptr(), n, ld, inf, sptr)
+        else:
+            st = plain_fn(copies[i].data_ptr(), n, ld, inf, sptr)
+        if st != ga.APSP_OK:
+            raise ga.APSPError(st, "apsp_fw warm-up")
+    torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
+    # Timed region: K asynchronous calls back to back, one synchronisation
+    # at the end.  The library's launch trace records HIP events around every
+    # launch of the last few calls on the calls' stream (no synchronisation
+    # in between); the per-kind times are read after the region.  Event
+    # markers cost about 4 us of idle GPU time per launch, so only a sample
+    # of the calls carries them (the Phase-3 average comes from 64 launches
+    # per traced call).
+    launches_per_call = 2 * nb + 8
+    n_traced = min(2, args.steps)
+    for _ in range(2):  # create the trace's event pool outside the region
+        if ga.apsp_trace_begin(n_traced * launches_per_call) != ga.APSP_OK:
+            raise RuntimeError("apsp_trace_begin failed")
+        ga.apsp_trace_end()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    phase_ms = [0.0] * 4
-    launches = [0] * 4
-    ariths = set()
-    ev0.record(stream)
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        ms, cnt, arith = step(copies[args.warmup + i])
-        ariths.add(arith)
-        for p in range(4):
-            phase_ms[p] += ms[p]
-            launches[p] += cnt[p]
-    ev1.record(stream)
+        if i == args.steps - n_traced:
+            st = ga.apsp_trace_begin(n_traced * launches_per_call)
+            if st != ga.APSP_OK:
+                raise ga.APSPError(st, "apsp_trace_begin")
+        st = plain_fn(copies[args.warmup + i].data_ptr(), n, ld, inf, sptr)
+        if st != ga.APSP_OK:
+            raise ga.APSPError(st, "apsp_fw")
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ev_ms = ev0.elapsed_time(ev1)
+    st, phase_ms, launches, dropped = ga.apsp_trace_end()
+    if st != ga.APSP_OK or dropped:
+        raise RuntimeError(f"launch trace failed: status {st}, {dropped} launches not recorded")
+    if arith_code is None:  # no warm-up: one extra synchronised call outside the region
+        scratch = torch.empty_like(pristine)
+        scratch.copy_(pristine)
+        _, _, _, arith_code = timed_fn(scratch.data_ptr(), n, ld, inf, sptr)
+        del scratch
     ms_per_step = 1e3 * wall / args.steps
     value = float(n) ** 3 / (wall / args.steps)
-    arith = "f32" if ariths == {1} else "int32" if ariths == {0} else "mixed"
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms, events {ev_ms:.1f} ms, "
-        f"ms/step by kind [phase1, phase2, phase3, scan+convert] "
-        f"{[round(x / args.steps, 3) for x in phase_ms]}, arithmetic {arith}")
+    arith = "f32" if arith_code == 1 else "int32"
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms; traced calls: ms/call by kind "
+        f"[phase1, phase2, phase3, scan+convert] "
+        f"{[round(x / n_traced, 3) for x in phase_ms]}, arithmetic {arith}")
 
     # Phase-3 roofline: algorithmic relaxations per launch / mean launch time.
-    p3_relax = sum(phase3_relaxations_per_round(n, B)) * args.steps
+    p3_relax = sum(phase3_relaxations_per_round(n, B)) * n_traced
     p3_launch = launches[2]
     p3_ms_avg = phase_ms[2] / max(p3_launch, 1)
     relax_per_launch = p3_relax / max(p3_launch, 1)
@@ -560,7 +583,8 @@ def main() -> int:
             "input_sha256": sha,
         },
         "ms_per_step_by_kind": dict(zip(["phase1", "phase2", "phase3", "scan_convert"],
-                                        [x / args.steps for x in phase_ms])),
+                                        [x / n_traced for x in phase_ms])),
+        "traced_steps": n_traced,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -11,17 +11,20 @@ streams are integers):
     apsp_fw_f32(d_ptr, n, ld, inf, stream) -> status
     apsp_fw_rounds_i32(d_ptr, n, ld, inf, r0, r1, stream) -> status
     apsp_fw_rounds_f32(d_ptr, n, ld, inf, r0, r1, stream) -> status
+    apsp_fw_signed_i32 / _f32(d_ptr, n, ld, inf, stream) -> status
     apsp_fw_timed_i32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
     apsp_fw_timed_f32(d_ptr, n, ld, inf, stream) -> (status, ms[4], launches[4], arith)
     apsp_fw_batched_i32 / _f32(d_ptr, batch, n, ld, stride, inf, stream) -> status
     apsp_johnson_i32(row_ptr, col, w, n, nnz, d_ptr, ld, inf, h_ptr, delta, stream) -> status
     apsp_johnson_timed_i32(...same...) -> (status, ms[4], counts[4])
+    apsp_trace_begin(max_launches), apsp_trace_end() -> (status, ms[4], launches[4], dropped)
     apsp_set_int32_arith(mode), apsp_get_int32_arith(), apsp_minplus_ceiling(arith)
     apsp_pivot_block(n), apsp_status_string(s), apsp_last_hip_error(), apsp_version()
 
 Tensor convenience:
     fw(t, inf=None)              in-place APSP of a 2-D int32/float32 CUDA tensor
     fw_rounds(t, r0, r1, inf=None)
+    fw_signed(t, inf=None)       in-place APSP with negative weights, synchronous
     fw_timed(t, inf=None)        -> (phase_ms, launches, arith), synchronised
     fw_batched(t, inf=None)      in-place APSP of every graph of a 3-D tensor
     johnson(row_ptr, col, w, out=None, inf=None, h=None, delta=-1)
@@ -55,7 +58,8 @@ EXPORTS = (
     "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
     "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
-    "apsp_johnson_timed_i32",
+    "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
+    "apsp_trace_begin", "apsp_trace_end",
 )
 
 _lib = None
@@ -111,6 +115,10 @@ def load(path: str | None = None):
         "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
         "apsp_fw_batched_i32": ([vp, i64, i64, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_batched_f32": ([vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_trace_begin": ([i64], ctypes.c_int),
+        "apsp_trace_end": ([dp, lp, lp], ctypes.c_int),
+        "apsp_fw_signed_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_fw_signed_f32": ([vp, i64, i64, f32, vp], ctypes.c_int),
         "apsp_johnson_i32": ([vp, vp, vp, i64, i64, vp, i64, i32, vp, i32, vp], ctypes.c_int),
         "apsp_johnson_timed_i32": ([vp, vp, vp, i64, i64, vp, i64, i32, vp, i32, vp, dp, lp],
                                    ctypes.c_int),
@@ -155,6 +163,27 @@ def apsp_fw_batched_i32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
 
 def apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
     return load().apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream)
+
+
+def apsp_trace_begin(max_launches: int) -> int:
+    return int(load().apsp_trace_begin(max_launches))
+
+
+def apsp_trace_end():
+    """(status, ms per kind [4], launches per kind [4], dropped launches)."""
+    ms = (ctypes.c_double * 4)()
+    cnt = (ctypes.c_int64 * 4)()
+    dropped = ctypes.c_int64(0)
+    st = load().apsp_trace_end(ms, cnt, ctypes.byref(dropped))
+    return int(st), list(ms), list(cnt), int(dropped.value)
+
+
+def apsp_fw_signed_i32(d_ptr, n, ld, inf, stream=0) -> int:
+    return load().apsp_fw_signed_i32(d_ptr or None, n, ld, inf, stream or None)
+
+
+def apsp_fw_signed_f32(d_ptr, n, ld, inf, stream=0) -> int:
+    return load().apsp_fw_signed_f32(d_ptr or None, n, ld, inf, stream or None)
 
 
 def apsp_johnson_i32(row_ptr, col, w, n, nnz, d_ptr, ld, inf, h_ptr=0, delta=-1, stream=0) -> int:
@@ -272,6 +301,18 @@ def fw(t, inf=None):
         st = (apsp_fw_i32 if kind == "i32" else apsp_fw_f32)(p, n, ld, inf, s)
     if st != APSP_OK:
         raise APSPError(st, "apsp_fw_" + kind)
+    return t
+
+
+def fw_signed(t, inf=None):
+    """In-place APSP of t[:n, :n] with negative weights allowed (synchronous).
+    Raises NegativeCycleError on a negative cycle."""
+    import torch
+    kind, p, n, ld, inf, s = _tensor_args(t, inf)
+    with torch.cuda.device(t.device):
+        st = (apsp_fw_signed_i32 if kind == "i32" else apsp_fw_signed_f32)(p, n, ld, inf, s)
+    if st != APSP_OK:
+        _raise(st, "apsp_fw_signed_" + kind)
     return t
 
 

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -659,6 +660,160 @@ fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64
 }
 
 // ---------------------------------------------------------------------------
+// Negative weights in the dense matrix (the setting of the Johnson's-APSP
+// page, where Floyd-Warshall must not treat "no edge" as a number).
+//
+// No guard is needed in the min-plus loops.  Let W be the largest |weight|
+// over finite off-diagonal entries and assume no negative cycle.
+//  * binary32: "no edge" becomes +infinity, and +inf plus any finite value
+//    is +inf, which is exactly the guard.  Every value the recurrence keeps
+//    is a walk length between -(n-1)W and (n-1)W, so when (n-1)W <= 2^24
+//    each is an exactly representable integer and, as for non-negative
+//    weights, the rounded minimum over the candidates is the exact one.
+//  * int32: "no edge" stays the number inf = M.  In the complete graph with
+//    weight M on non-edges, a simple path that uses a non-edge weighs at
+//    least M - (n-2)W, and a cycle that uses one weighs at least
+//    M - (n-1)W > 0, so that graph has no negative cycle either.  Its
+//    shortest distances equal the true ones (at most (n-1)W) on reachable
+//    pairs when M > (2n-3)W, and exceed (n-1)W on the others.  The plain
+//    recurrence computes them without overflow (values stay in
+//    [-(n-1)W, M], sums in [-2(n-1)W, 2M]); a final pass maps every value
+//    above (n-1)W back to inf.  With no non-edge at all the same holds when
+//    (n-1)W < 2^30.
+// A negative cycle shows as some d(i, i) < 0 after the rounds (a stored
+// value never increases, so a negative diagonal stays negative).
+// ---------------------------------------------------------------------------
+constexpr int32_t kSgHasInf = 1;      // an off-diagonal entry equals inf
+constexpr int32_t kSgBadEntry = 2;    // a diagonal entry != 0, or an entry outside (-inf, inf]
+struct SignedScan {
+  int32_t maxabs;     // largest |finite off-diagonal entry|
+  int32_t flags;
+  int32_t neg_cycle;  // some d(i, i) < 0 after the rounds
+  int32_t pad;
+};
+
+__global__ void __launch_bounds__(64) signed_zero(SignedScan* __restrict__ s) {
+  if (threadIdx.x == 0) *s = SignedScan{0, 0, 0, 0};
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) scan_signed_i32(const int32_t* __restrict__ d,
+                                                            int64_t n, int64_t ld, int32_t inf,
+                                                            SignedScan* __restrict__ s) {
+  int32_t mx = 0, fl = 0;
+  auto visit = [&](int32_t v, int64_t r, int64_t c) {
+    if (r == c) {
+      if (v != 0) fl |= kSgBadEntry;
+    } else if (v == inf) {
+      fl |= kSgHasInf;
+    } else if (v > inf || v <= -inf) {
+      fl |= kSgBadEntry;
+    } else {
+      mx = max(mx, v < 0 ? -v : v);
+    }
+  };
+  const int64_t quads = (n + 3) / 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int32_t* row = d + r * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t c = q * 4;
+      if (VEC && c + 3 < n) {
+        int32_t v[4];
+        load4(row + c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) visit(v[e], r, c + e);
+      } else {
+        for (int e = 0; e < 4 && c + e < n; ++e) visit(row[c + e], r, c + e);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o));
+    fl |= __shfl_xor(fl, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    if (mx) atomicMax(&s->maxabs, mx);
+    if (fl) atomicOr(&s->flags, fl);
+  }
+}
+
+// In place: int32 entries <-> binary32 (inf <-> +infinity).  Back from
+// binary32, anything >= inf (including +inf) is inf; values below -2^31
+// (possible only after a negative cycle) saturate.
+template <bool VEC, bool TO_F32>
+__global__ void __launch_bounds__(kThreads) signed_convert(int32_t* __restrict__ d, int64_t n,
+                                                           int64_t ld, int32_t inf) {
+  const float finf = (float)inf;
+  auto conv = [&](int32_t v) -> int32_t {
+    if (TO_F32) return __float_as_int(v == inf ? __builtin_inff() : (float)v);
+    const float f = __int_as_float(v);
+    if (f >= finf) return inf;
+    if (!(f > -2147483648.0f)) return INT32_MIN;  // also catches NaN
+    return (int32_t)f;
+  };
+  const int64_t quads = (n + 3) / 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    int32_t* row = d + r * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t c = q * 4;
+      if (VEC && c + 3 < n) {
+        int32_t v[4];
+        load4(row + c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = conv(v[e]);
+        store4(row + c, v);
+      } else {
+        for (int e = 0; e < 4 && c + e < n; ++e) row[c + e] = conv(row[c + e]);
+      }
+    }
+  }
+}
+
+// In place: every value above thr becomes inf (the int32 form above).
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) signed_clamp(int32_t* __restrict__ d, int64_t n,
+                                                         int64_t ld, int32_t inf, int32_t thr) {
+  const int64_t quads = (n + 3) / 4;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    int32_t* row = d + r * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+      const int64_t c = q * 4;
+      if (VEC && c + 3 < n) {
+        int32_t v[4];
+        load4(row + c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = v[e] > thr ? inf : v[e];
+        store4(row + c, v);
+      } else {
+        for (int e = 0; e < 4 && c + e < n; ++e) row[c + e] = row[c + e] > thr ? inf : row[c + e];
+      }
+    }
+  }
+}
+
+// float32 matrices: the caller's sentinel <-> +infinity, in place.
+template <bool TO_INF>
+__global__ void __launch_bounds__(kThreads) signed_sentinel_f32(float* __restrict__ d, int64_t n,
+                                                                int64_t ld, float inf) {
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    float* row = d + r * ld;
+    for (int64_t c = threadIdx.x; c < n; c += kThreads) {
+      const float v = row[c];
+      if (TO_INF ? v == inf : v >= inf) row[c] = TO_INF ? __builtin_inff() : inf;
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) diag_negative(const T* __restrict__ d, int64_t n,
+                                                          int64_t ld, SignedScan* __restrict__ s) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    if (d[i * ld + i] < T(0)) s->neg_cycle = 1;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 thread_local int g_last_hip_error = 0;
@@ -724,11 +879,16 @@ enum { kKindPhase1 = 0, kKindPhase2 = 1, kKindPhase3 = 2, kKindConvert = 3, kKin
 
 struct PhaseTimer {
   // Events bracketing each launch: ev[2*i] before, ev[2*i+1] after launch i.
+  // Launches beyond `cap` are not recorded (counted in `dropped`).
   hipEvent_t* ev = nullptr;
   int* kind = nullptr;
-  int64_t cap = 0, used = 0;
+  int64_t cap = 0, used = 0, dropped = 0;
   hipStream_t s = nullptr;
   void mark(int k, bool before) {
+    if (used >= cap) {
+      if (!before) ++dropped;
+      return;
+    }
     if (before) {
       (void)hipEventRecord(ev[2 * used], s);
       kind[used] = k;
@@ -738,6 +898,19 @@ struct PhaseTimer {
     }
   }
 };
+
+// Launch tracing across calls (apsp_trace_begin / apsp_trace_end): while it
+// is on, every Floyd-Warshall call of this thread records events around its
+// launches into one pooled buffer, with no synchronisation; the totals are
+// read once at the end.
+struct Trace {
+  bool on = false;
+  int dev = -1;
+  hipEvent_t* ev = nullptr;  // 2 * cap events, owned by the event pool
+  int* kind = nullptr;
+  int64_t cap = 0, used = 0, dropped = 0;
+};
+thread_local Trace g_trace;
 
 int launch_status() {
   hipError_t e = hipGetLastError();
@@ -826,8 +999,24 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
   st = check_device();
   if (st != APSP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PhaseTimer trace_tm;
+  if (!tm && g_trace.on) {
+    trace_tm.ev = g_trace.ev + 2 * g_trace.used;
+    trace_tm.kind = g_trace.kind + g_trace.used;
+    trace_tm.cap = g_trace.cap - g_trace.used;
+    tm = &trace_tm;
+  }
   if (tm) tm->s = s;
   const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+  struct TraceCommit {  // fold the launches of this call into the trace
+    PhaseTimer* t;
+    ~TraceCommit() {
+      if (t) {
+        g_trace.used += t->used;
+        g_trace.dropped += t->dropped;
+      }
+    }
+  } commit{tm == &trace_tm ? &trace_tm : nullptr};
   if constexpr (std::is_same_v<T, int32_t>) {
     // Binary32 pays only when Phase 3 keeps two workgroups on every CU (its
     // double issue rate needs several waves per SIMD); smaller matrices stay in
@@ -869,10 +1058,10 @@ struct EventPool {
 };
 thread_local EventPool g_event_pool[kMaxDevices];
 
-hipEvent_t* pooled_events(int64_t count) {
+hipEvent_t* grow_pool(EventPool* pools, int64_t count) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  EventPool& p = g_event_pool[dev];
+  EventPool& p = pools[dev];
   if (p.size >= count) return p.ev;
   hipEvent_t* ev = new hipEvent_t[count];
   for (int64_t i = 0; i < p.size; ++i) ev[i] = p.ev[i];
@@ -884,6 +1073,12 @@ hipEvent_t* pooled_events(int64_t count) {
   p.size = made;
   return made >= count ? ev : nullptr;
 }
+
+// The timed entry points and the cross-call trace keep separate pools, so a
+// timed call made while a trace is on cannot move the trace's events.
+thread_local EventPool g_trace_pool[kMaxDevices];
+
+hipEvent_t* pooled_events(int64_t count) { return grow_pool(g_event_pool, count); }
 
 template <typename T>
 int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms,
@@ -931,6 +1126,124 @@ int run_timed(T* d, int64_t n, int64_t ld, T inf, void* stream, double* phase_ms
   return st;
 }
 
+// A failed HIP call: keep its error for apsp_last_hip_error.
+int hip_failed() {
+  g_last_hip_error = (int)hipGetLastError();
+  return APSP_ERR_LAUNCH;
+}
+
+int sync_read(hipStream_t s, void* host, const void* dev, size_t bytes) {
+  if (hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return hip_failed();
+  return APSP_OK;
+}
+
+// Negative weights, int32 matrix (see the kernels above).  Synchronous.
+int run_signed_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream, int* arith_out) {
+  if (arith_out) *arith_out = -1;
+  int st = validate<int32_t>(d, n, ld, inf);
+  if (st != APSP_OK || n == 0) return st;
+  st = check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+  const int64_t nb = (n + kB - 1) / kB;
+  const unsigned rows = (unsigned)(n < kScanBlocks ? n : kScanBlocks);
+  SignedScan* sc = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&sc), sizeof(SignedScan), s) != hipSuccess)
+    return hip_failed();
+  SignedScan h{};
+  int rc = APSP_OK;
+  do {
+    hipLaunchKernelGGL(signed_zero, dim3(1), dim3(64), 0, s, sc);
+    if (vec) hipLaunchKernelGGL((scan_signed_i32<true>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf, sc);
+    else hipLaunchKernelGGL((scan_signed_i32<false>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf, sc);
+    if ((rc = launch_status()) != APSP_OK || (rc = sync_read(s, &h, sc, sizeof(h))) != APSP_OK) break;
+    if (h.flags & kSgBadEntry) {
+      rc = APSP_ERR_INVALID_VALUE;
+      break;
+    }
+    const int64_t W = h.maxabs;
+    const bool has_inf = (h.flags & kSgHasInf) != 0;
+    const int policy = g_int32_arith.load(std::memory_order_relaxed);
+    const int64_t tiles = (nb - 1) * (nb - 1);
+    const bool exact_f32 = (n - 1) * W <= kExactLimit && policy != APSP_ARITH_INT32;
+    const bool prefer_f32 = policy == APSP_ARITH_F32_WHEN_EXACT ||
+                            (policy == APSP_ARITH_AUTO && tiles >= (int64_t)kP3PerCu * device_cus());
+    const bool i32_ok = has_inf ? (2 * n - 3) * W < (int64_t)inf : (n - 1) * W < (int64_t(1) << 30);
+    if (!exact_f32 && !i32_ok) {
+      rc = APSP_ERR_RANGE;
+      break;
+    }
+    const bool f32 = exact_f32 && (prefer_f32 || !i32_ok);
+    if (arith_out) *arith_out = f32 ? 1 : 0;
+    if (f32) {
+      float* fd = reinterpret_cast<float*>(d);
+      if (vec) {
+        hipLaunchKernelGGL((signed_convert<true, true>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+        enqueue_rounds<float, true>(fd, n, ld, __builtin_inff(), 0, nb, s, nullptr, nullptr);
+        hipLaunchKernelGGL((signed_convert<true, false>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+      } else {
+        hipLaunchKernelGGL((signed_convert<false, true>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+        enqueue_rounds<float, false>(fd, n, ld, __builtin_inff(), 0, nb, s, nullptr, nullptr);
+        hipLaunchKernelGGL((signed_convert<false, false>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+      }
+    } else {
+      const int32_t thr = (int32_t)((n - 1) * W);
+      if (vec) {
+        enqueue_rounds<int32_t, true>(d, n, ld, inf, 0, nb, s, nullptr, nullptr);
+        if (has_inf) hipLaunchKernelGGL((signed_clamp<true>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf, thr);
+      } else {
+        enqueue_rounds<int32_t, false>(d, n, ld, inf, 0, nb, s, nullptr, nullptr);
+        if (has_inf) hipLaunchKernelGGL((signed_clamp<false>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf, thr);
+      }
+    }
+    const unsigned dg = (unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
+    hipLaunchKernelGGL((diag_negative<int32_t>), dim3(dg), dim3(kThreads), 0, s, d, n, ld, sc);
+    if ((rc = launch_status()) != APSP_OK || (rc = sync_read(s, &h, sc, sizeof(h))) != APSP_OK) break;
+    if (h.neg_cycle) rc = APSP_ERR_NEGATIVE_CYCLE;
+  } while (false);
+  (void)hipFreeAsync(sc, s);
+  (void)hipStreamSynchronize(s);
+  return rc;
+}
+
+// Negative weights, float32 matrix: the sentinel becomes +infinity for the
+// rounds, which makes every sum through it +infinity.  Synchronous.
+int run_signed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
+  int st = validate<float>(d, n, ld, inf);
+  if (st != APSP_OK || n == 0) return st;
+  st = check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+  const int64_t nb = (n + kB - 1) / kB;
+  const unsigned rows = (unsigned)(n < kScanBlocks ? n : kScanBlocks);
+  SignedScan* sc = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&sc), sizeof(SignedScan), s) != hipSuccess)
+    return hip_failed();
+  SignedScan h{};
+  int rc = APSP_OK;
+  do {
+    hipLaunchKernelGGL(signed_zero, dim3(1), dim3(64), 0, s, sc);
+    const bool finite = inf != __builtin_inff();
+    if (finite)
+      hipLaunchKernelGGL((signed_sentinel_f32<true>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+    if (vec) enqueue_rounds<float, true>(d, n, ld, __builtin_inff(), 0, nb, s, nullptr, nullptr);
+    else enqueue_rounds<float, false>(d, n, ld, __builtin_inff(), 0, nb, s, nullptr, nullptr);
+    if (finite)
+      hipLaunchKernelGGL((signed_sentinel_f32<false>), dim3(rows), dim3(kThreads), 0, s, d, n, ld, inf);
+    const unsigned dg = (unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
+    hipLaunchKernelGGL((diag_negative<float>), dim3(dg), dim3(kThreads), 0, s, d, n, ld, sc);
+    if ((rc = launch_status()) != APSP_OK || (rc = sync_read(s, &h, sc, sizeof(h))) != APSP_OK) break;
+    if (h.neg_cycle) rc = APSP_ERR_NEGATIVE_CYCLE;
+  } while (false);
+  (void)hipFreeAsync(sc, s);
+  (void)hipStreamSynchronize(s);
+  return rc;
+}
+
 }  // namespace
 
 // Library-internal host helpers for the other translation units.
@@ -967,6 +1280,60 @@ int apsp_fw_timed_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stre
 int apsp_fw_timed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream,
                       double* phase_ms, int64_t* phase_launch, int* arith) {
   return run_timed<float>(d, n, ld, inf, stream, phase_ms, phase_launch, arith);
+}
+
+int apsp_fw_signed_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream) {
+  return run_signed_i32(d, n, ld, inf, stream, nullptr);
+}
+
+int apsp_fw_signed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
+  return run_signed_f32(d, n, ld, inf, stream);
+}
+
+int apsp_trace_begin(int64_t max_launches) {
+  if (max_launches <= 0 || max_launches > (int64_t(1) << 24)) return APSP_ERR_INVALID_VALUE;
+  if (g_trace.on) return APSP_ERR_INVALID_VALUE;
+  int st = check_device();
+  if (st != APSP_OK) return st;
+  hipEvent_t* ev = grow_pool(g_trace_pool, 2 * max_launches);
+  if (ev == nullptr) return hip_failed();
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  delete[] g_trace.kind;
+  g_trace.kind = new int[max_launches];
+  g_trace.ev = ev;
+  g_trace.cap = max_launches;
+  g_trace.used = g_trace.dropped = 0;
+  g_trace.dev = dev;
+  g_trace.on = true;
+  return APSP_OK;
+}
+
+int apsp_trace_end(double* phase_ms, int64_t* phase_launch, int64_t* dropped) {
+  if (phase_ms) for (int p = 0; p < kKinds; ++p) phase_ms[p] = 0.0;
+  if (phase_launch) for (int p = 0; p < kKinds; ++p) phase_launch[p] = 0;
+  if (dropped) *dropped = 0;
+  if (!g_trace.on) return APSP_ERR_INVALID_VALUE;
+  g_trace.on = false;
+  int rc = APSP_OK;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  if (cur != g_trace.dev) (void)hipSetDevice(g_trace.dev);
+  if (g_trace.used > 0 && hipEventSynchronize(g_trace.ev[2 * g_trace.used - 1]) != hipSuccess)
+    rc = hip_failed();
+  for (int64_t i = 0; rc == APSP_OK && i < g_trace.used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess) {
+      rc = hip_failed();
+      break;
+    }
+    const int p = g_trace.kind[i];
+    if (phase_ms) phase_ms[p] += ms;
+    if (phase_launch) phase_launch[p] += 1;
+  }
+  if (dropped) *dropped = g_trace.dropped;
+  if (cur != g_trace.dev) (void)hipSetDevice(cur);
+  return rc;
 }
 
 int apsp_set_int32_arith(int mode) {

@@ -89,6 +89,33 @@ int apsp_fw_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream);
 int apsp_fw_f32(float *d, int64_t n, int64_t ld, float inf, void *stream);
 
 /*
+ * All-pairs shortest paths of a dense matrix whose weights may be negative
+ * (the setting of the page "Johnson's APSP in Glushkov algorithmic
+ * algebras", where a path through "no edge" must never count): in place, the
+ * same blocked rounds ("Katz and Kider" page, section 4.6), no sum ever
+ * passes through the sentinel.
+ * Input: d[i][i] = 0; off-diagonal entries are weights in (-inf, inf) or
+ * exactly inf ("no edge").  int32: 1 <= inf <= 0x3FFFFFFF.  float32: inf > 0
+ * or +infinity; weights finite.
+ * int32 arithmetic (W = the largest |weight|): binary32 with "no edge" as
+ * +infinity when (n - 1) * W <= 2^24 (exact, as for apsp_fw_i32; subject to
+ * the arithmetic policy below); else int32 with the sentinel as a large
+ * number, exact when (2n - 3) * W < inf (or (n - 1) * W < 2^30 when no entry
+ * is inf), followed by a pass that restores inf on unreachable pairs.
+ * Otherwise APSP_ERR_RANGE before anything is written.  float32: the
+ * sentinel becomes +infinity for the rounds and comes back as inf; results
+ * as for apsp_fw_f32.
+ * Returns APSP_ERR_INVALID_VALUE (nothing written) for a non-zero diagonal
+ * entry or an int32 entry outside (-inf, inf] (checked on the device), and
+ * APSP_ERR_NEGATIVE_CYCLE when some d[i][i] < 0 after the rounds (a negative
+ * cycle through i); d then holds the unspecified partial results.
+ * Synchronous: returns after the work on `stream` has completed.  Takes 16
+ * bytes of stream-ordered scratch.  Other errors as for apsp_fw_i32.
+ */
+int apsp_fw_signed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream);
+int apsp_fw_signed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream);
+
+/*
  * Rounds [round_begin, round_end) only, in place, with pivot blocks of
  * apsp_pivot_block(n) vertices; round r uses pivots [r*B, min((r+1)*B, n)).
  * After rounds [0, r) the matrix holds the shortest distances over paths
@@ -120,6 +147,22 @@ int apsp_fw_timed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stre
                       double *phase_ms, int64_t *phase_launch, int *arith);
 int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
                       double *phase_ms, int64_t *phase_launch, int *arith);
+
+/*
+ * Measurement across calls: after apsp_trace_begin(max_launches), every
+ * apsp_fw_i32 / apsp_fw_f32 / apsp_fw_rounds_* call made by this thread
+ * records HIP events around each launch (or launch group, as for
+ * apsp_fw_timed_i32), on the call's stream, without synchronising.
+ * apsp_trace_end synchronises on the last recorded event, ends the trace and
+ * writes the summed event time and the number of launches per kind (the
+ * kinds of apsp_fw_timed_i32) and the number of launches beyond max_launches
+ * that were not recorded (any pointer may be NULL).  Events come from a
+ * per-thread pool that lives until the process ends.  apsp_trace_begin
+ * returns APSP_ERR_INVALID_VALUE for max_launches outside [1, 2^24] or when
+ * a trace is already on; apsp_trace_end returns it when none is on.
+ */
+int apsp_trace_begin(int64_t max_launches);
+int apsp_trace_end(double *phase_ms, int64_t *phase_launch, int64_t *dropped);
 
 /*
  * Many small graphs at once: all-pairs shortest paths of `batch` independent

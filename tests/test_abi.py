@@ -174,3 +174,26 @@ def test_johnson_empty_graph_is_a_no_op(lib):
 def test_status_strings_for_negative_weights(lib):
     assert "NEGATIVE_CYCLE" in ga.apsp_status_string(ga.APSP_ERR_NEGATIVE_CYCLE)
     assert "RANGE" in ga.apsp_status_string(ga.APSP_ERR_RANGE)
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, -1, 4, 100), (0, 4, 4, 100), (FAKE, 8, 7, 100), (FAKE + 2, 4, 4, 100),
+    (FAKE, 4, 4, 0), (FAKE, 4, 4, 0x40000000),
+])
+def test_signed_argument_errors(lib, args):
+    assert ga.apsp_fw_signed_i32(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_signed_f32_bad_inf_and_empty(lib):
+    for inf in (0.0, -1.0, float("nan")):
+        assert ga.apsp_fw_signed_f32(FAKE, 4, 4, inf, 0) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_fw_signed_i32(0, 0, 1, 100, 0) == ga.APSP_OK
+    assert ga.apsp_fw_signed_f32(0, 0, 1, 1.0, 0) == ga.APSP_OK
+
+
+def test_trace_argument_errors(lib):
+    assert ga.apsp_trace_begin(0) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_trace_begin(-5) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_trace_begin((1 << 24) + 1) == ga.APSP_ERR_INVALID_VALUE
+    st, ms, cnt, dropped = ga.apsp_trace_end()        # none is on
+    assert st == ga.APSP_ERR_INVALID_VALUE and cnt == [0, 0, 0, 0] and dropped == 0

@@ -298,3 +298,40 @@ def test_minplus_ceiling_diagnostic(torch_dev):
     st, rf = ga.apsp_minplus_ceiling(1)
     assert st == ga.APSP_OK and 0.5 * 5.24e13 < rf < 2.0 * 5.24e13
     assert ga.apsp_minplus_ceiling(5)[0] == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_trace_across_calls_counts_every_launch(torch_dev):
+    # three asynchronous calls under one trace record exactly three times the
+    # launches (and launch groups) of one synchronised timed call, and the
+    # results are unchanged
+    print("case trace across calls", flush=True)
+    torch, dev = torch_dev
+    n = 1000
+    w = gg.erdos_renyi(n, 0.01, 1, 100, 41)
+    want = oracle.fw_i32(w)
+    s = torch.cuda.current_stream().cuda_stream
+    per_call = {}
+    for mode in (ga.APSP_ARITH_AUTO, ga.APSP_ARITH_F32_WHEN_EXACT):
+        with ga.int32_arith(mode):
+            one = torch.from_numpy(w).to(dev)
+            st, _, cnt1, _ = ga.apsp_fw_timed_i32(one.data_ptr(), n, n, INF, s)
+            assert st == ga.APSP_OK
+            per_call[mode] = sum(cnt1)
+            ts = [torch.from_numpy(w).to(dev) for _ in range(3)]
+            torch.cuda.synchronize()
+            assert ga.apsp_trace_begin(1000) == ga.APSP_OK
+            assert ga.apsp_trace_begin(10) == ga.APSP_ERR_INVALID_VALUE  # already on
+            for t in ts:
+                assert ga.apsp_fw_i32(t.data_ptr(), n, n, INF, s) == ga.APSP_OK
+            st, ms, cnt, dropped = ga.apsp_trace_end()
+            assert st == ga.APSP_OK and dropped == 0
+            assert cnt == [3 * c for c in cnt1] and all(x >= 0 for x in ms) and ms[2] > 0
+            for t in ts:
+                assert np.array_equal(t.cpu().numpy(), want)
+    # a trace smaller than the launches keeps the first ones and counts the rest
+    t = torch.from_numpy(w).to(dev)
+    assert ga.apsp_trace_begin(5) == ga.APSP_OK
+    assert ga.apsp_fw_i32(t.data_ptr(), n, n, INF, s) == ga.APSP_OK
+    st, ms, cnt, dropped = ga.apsp_trace_end()
+    assert st == ga.APSP_OK and sum(cnt) == 5 and dropped == per_call[ga.APSP_ARITH_AUTO] - 5
+    assert np.array_equal(t.cpu().numpy(), want)

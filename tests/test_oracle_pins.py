@@ -407,3 +407,20 @@ def test_johnson_potentials_flag_any_negative_cycle(orc):
     w[3, 4], w[4, 3] = 1, -2
     rp, c, wt = _csr(w)
     assert orc.johnson_potentials(rp, c, wt, 5)[1]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_float_fw_with_ieee_inf_handles_negative_weights(orc, seed):
+    # with +infinity as "no edge", inf + (negative) stays inf, so the plain
+    # binary64 recurrence is already guarded: it must equal brute force
+    rng = np.random.default_rng(45000 + seed)
+    n = int(rng.integers(1, 8))
+    w0 = random_small_graph(rng, n, [0.3, 0.6][seed % 2], 4, np.inf, floats=True)
+    pot = rng.uniform(-2.0, 2.0, size=n)
+    edge = np.isfinite(w0) & ~np.eye(n, dtype=bool)
+    w = np.where(edge, w0 + pot[:, None] - pot[None, :], w0)
+    want = brute_force_apsp(w, np.inf).astype(np.float64)
+    got = orc.fw_f64(w)
+    assert np.array_equal(np.isinf(got), np.isinf(want))
+    fin = np.isfinite(want)
+    assert np.allclose(got[fin], want[fin], rtol=1e-12, atol=1e-12)
