@@ -76,13 +76,16 @@ def phase3_relaxations_per_round(n: int, B: int) -> list[int]:
     return out
 
 
-def source_sha(name: str = "apsp.hip") -> str:
-    p = os.path.join(ROOT, "graph_all_pairs_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+def source_sha(names=("apsp.hip", "minplus.h")) -> str:
+    """SHA-256 over the kernel sources a counter summary was taken on."""
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "graph_all_pairs_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def read_traffic(workload: str, per_launch_relax: float, kernel: str = "phase3",
-                 source: str = "apsp.hip"):
+                 source=("apsp.hip", "minplus.h")):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary, when it was taken on the current kernel
     source; else None."""
@@ -221,7 +224,8 @@ def bench_batched(args) -> int:
         "peak": peak / 1e12,
         "unit": "Trelax/s",
         "frac": achieved / peak,
-        "traffic": read_traffic(args.workload, relax, kernel="batched", source="batched.hip"),
+        "traffic": read_traffic(args.workload, relax, kernel="batched",
+                                source=("batched.hip", "minplus.h")),
         "relax_per_launch": relax,
         "avg_launch_ms": kern_ms,
         "launches": args.steps,
