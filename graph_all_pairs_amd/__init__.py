@@ -59,7 +59,8 @@ EXPORTS = (
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
     "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
     "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
-    "apsp_trace_begin", "apsp_trace_end",
+    "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
+    "apsp_fw_host_i32", "apsp_fw_host_f32",
 )
 
 _lib = None
@@ -115,6 +116,10 @@ def load(path: str | None = None):
         "apsp_fw_timed_f32": ([vp, i64, i64, f32, vp, dp, lp, ip], ctypes.c_int),
         "apsp_fw_batched_i32": ([vp, i64, i64, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_batched_f32": ([vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_minplus_gemm_i32": ([vp, i64, vp, i64, vp, i64, i64, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_minplus_gemm_f32": ([vp, i64, vp, i64, vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_fw_host_i32": ([vp, i64, i64, i32, i64, vp, lp], ctypes.c_int),
+        "apsp_fw_host_f32": ([vp, i64, i64, f32, i64, vp, lp], ctypes.c_int),
         "apsp_trace_begin": ([i64], ctypes.c_int),
         "apsp_trace_end": ([dp, lp, lp], ctypes.c_int),
         "apsp_fw_signed_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
@@ -163,6 +168,31 @@ def apsp_fw_batched_i32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
 
 def apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream=0) -> int:
     return load().apsp_fw_batched_f32(d_ptr, batch, n, ld, stride, inf, stream)
+
+
+def apsp_minplus_gemm_i32(c, ldc, a, lda, b, ldb, m, n, k, inf, stream=0) -> int:
+    return load().apsp_minplus_gemm_i32(c or None, ldc, a or None, lda, b or None, ldb, m, n, k,
+                                        inf, stream or None)
+
+
+def apsp_minplus_gemm_f32(c, ldc, a, lda, b, ldb, m, n, k, inf, stream=0) -> int:
+    return load().apsp_minplus_gemm_f32(c or None, ldc, a or None, lda, b or None, ldb, m, n, k,
+                                        inf, stream or None)
+
+
+def apsp_fw_host_i32(h_ptr, n, ld, inf, device_bytes=0, stream=0):
+    """(status, outer block S used)."""
+    blk = ctypes.c_int64(0)
+    st = load().apsp_fw_host_i32(h_ptr or None, n, ld, inf, device_bytes, stream or None,
+                                 ctypes.byref(blk))
+    return int(st), int(blk.value)
+
+
+def apsp_fw_host_f32(h_ptr, n, ld, inf, device_bytes=0, stream=0):
+    blk = ctypes.c_int64(0)
+    st = load().apsp_fw_host_f32(h_ptr or None, n, ld, inf, device_bytes, stream or None,
+                                 ctypes.byref(blk))
+    return int(st), int(blk.value)
 
 
 def apsp_trace_begin(max_launches: int) -> int:
@@ -405,3 +435,50 @@ def johnson(row_ptr, col, w, out=None, inf=None, h=None, delta=-1, timed=False):
     if st != APSP_OK:
         _raise(st, "apsp_johnson_i32")
     return (out, ms, counts) if timed else out
+
+
+def minplus_gemm(c, a, b, inf=None):
+    """c <- min(c, a (x) b) for 2-D CUDA tensors (rows contiguous, same dtype
+    int32 or float32), on the current stream."""
+    import torch
+    for t in (c, a, b):
+        if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError("operands must be 2-D CUDA tensors with contiguous rows")
+    if not (c.dtype == a.dtype == b.dtype) or c.dtype not in (torch.int32, torch.float32):
+        raise ValueError("operands must share dtype int32 or float32")
+    m, n, k = c.shape[0], c.shape[1], a.shape[1]
+    if a.shape[0] != m or b.shape[0] != k or b.shape[1] != n:
+        raise ValueError("shapes must be c (m, n), a (m, k), b (k, n)")
+    ld = lambda t: max(t.stride(0), t.shape[1], 1)
+    is_int = c.dtype == torch.int32
+    inf = (INF_I32 if is_int else float("inf")) if inf is None else inf
+    fn = apsp_minplus_gemm_i32 if is_int else apsp_minplus_gemm_f32
+    with torch.cuda.device(c.device):
+        st = fn(c.data_ptr(), ld(c), a.data_ptr(), ld(a), b.data_ptr(), ld(b), m, n, k, inf,
+                torch.cuda.current_stream(c.device).cuda_stream)
+    if st != APSP_OK:
+        _raise(st, "apsp_minplus_gemm")
+    return c
+
+
+def fw_host(t, inf=None, device_bytes=0):
+    """In-place APSP of a 2-D int32/float32 CPU tensor (pin it for speed),
+    streamed through the GPU in outer blocks; returns the outer block used."""
+    import torch
+    if t.is_cuda or t.dim() != 2 or t.shape[1] < t.shape[0]:
+        raise ValueError("expected a 2-D host tensor with at least n columns")
+    n = t.shape[0]
+    if n > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous")
+    ld = t.stride(0) if n > 1 else max(t.shape[1], 1)
+    if t.dtype == torch.int32:
+        fn, inf = apsp_fw_host_i32, (INF_I32 if inf is None else int(inf))
+    elif t.dtype == torch.float32:
+        fn, inf = apsp_fw_host_f32, (float("inf") if inf is None else float(inf))
+    else:
+        raise ValueError("dtype must be int32 or float32")
+    st, blk = fn(t.data_ptr(), n, ld, inf, device_bytes,
+                 torch.cuda.current_stream().cuda_stream)
+    if st != APSP_OK:
+        _raise(st, "apsp_fw_host")
+    return blk

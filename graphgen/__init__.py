@@ -145,9 +145,16 @@ def erdos_renyi(n: int, p: float, wlo: int, whi: int, seed: int,
 
 
 def complete(n: int, wlo: int, whi: int, seed: int, inf: int = INF_I32,
-             ld: int | None = None, canary: int = -7) -> np.ndarray:
-    """Complete digraph with integer weights uniform on [wlo, whi] (int32)."""
-    m = _alloc(n, ld, np.int32, inf, canary)
+             ld: int | None = None, canary: int = -7, out: np.ndarray | None = None) -> np.ndarray:
+    """Complete digraph with integer weights uniform on [wlo, whi] (int32).
+    With ``out`` (an int32 array of shape (n, >= n), e.g. a view of pinned
+    host memory) the matrix is written there in row chunks."""
+    if out is not None:
+        if out.dtype != np.int32 or out.ndim != 2 or out.shape[0] != n or out.shape[1] < n:
+            raise ValueError("out must be an int32 (n, >= n) array")
+        m = out
+    else:
+        m = _alloc(n, ld, np.int32, inf, canary)
     j = np.arange(n, dtype=np.uint64)
     for r0, r1 in _rows_chunks(n):
         i = np.arange(r0, r1, dtype=np.uint64)[:, None]
@@ -412,6 +419,13 @@ WORKLOADS = {
     "complete-8192-i32": dict(kind="complete", n=8192, wlo=1, whi=10000, seed=3, dtype="i32"),
     "ba-16000-b8-i32": dict(kind="ba", n=16000, beta=8, wlo=1, whi=255, seed=4, dtype="i32"),
     "complete-12288-f32": dict(kind="complete_f32", n=12288, seed=5, dtype="f32"),
+}
+
+# Host-resident matrices for the out-of-core path: the matrix stays in
+# (pinned) host memory and streams through a device budget smaller than it.
+HOST_WORKLOADS = {
+    "host-complete-32768-i32": dict(kind="complete", n=32768, wlo=1, whi=10000, seed=6,
+                                    outer_block=8192),
 }
 
 

@@ -149,6 +149,59 @@ int apsp_fw_timed_f32(float *d, int64_t n, int64_t ld, float inf, void *stream,
                       double *phase_ms, int64_t *phase_launch, int *arith);
 
 /*
+ * Min-plus matrix product C <- min(C, A (x) B), (A (x) B)[i][j] = min over t
+ * of A[i][t] + B[t][j]: the update inside Phases 2 and 3 of the "Katz and
+ * Kider" page (thesis section 4.6, Algorithms 17 and 18), for operands in
+ * separate device buffers and of any depth k.
+ *   C  m x n, element (i, j) at C[i*ldc + j], ldc >= n;
+ *   A  m x k, at A[i*lda + t], lda >= k;   B  k x n, at B[t*ldb + j], ldb >= n.
+ * Device pointers, 4-byte aligned (128-bit access when all three are 16-byte
+ * aligned and every leading dimension is a multiple of 4).  C must not
+ * overlap A or B.  m, n or k = 0 is a no-op.
+ * int32 entries lie in [0, inf] with 1 <= inf <= 0x3FFFFFFF (sums cannot
+ * overflow, and inf + x never improves an entry).  float32 entries are <=
+ * inf (inf > 0 or +infinity); with +infinity as "no path", finite entries
+ * may be negative (+infinity plus anything finite stays +infinity).  int32 results are exact; float32 results are
+ * each the minimum of single rounded sums (deterministic).  Asynchronous on
+ * `stream`; allocates nothing.  Errors: APSP_ERR_INVALID_VALUE for bad
+ * arguments before any HIP call, else as for apsp_fw_i32.
+ */
+int apsp_minplus_gemm_i32(int32_t *C, int64_t ldc, const int32_t *A, int64_t lda,
+                          const int32_t *B, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                          int32_t inf, void *stream);
+int apsp_minplus_gemm_f32(float *C, int64_t ldc, const float *A, int64_t lda, const float *B,
+                          int64_t ldb, int64_t m, int64_t n, int64_t k, float inf, void *stream);
+
+/*
+ * All-pairs shortest paths of a matrix in HOST memory, for graphs larger
+ * than device memory ("Katz and Kider" page, section 4.6.1: the in-core
+ * method needs the whole graph in global memory).  The blocked rounds run on
+ * outer blocks of S pivots (S a multiple of 128, the largest that fits the
+ * device budget): the S x S diagonal block is closed on the device by the
+ * in-core rounds, the S-wide pivot-row and pivot-column panels are updated
+ * and held in device memory, and every other S x S super-tile streams to the
+ * device, takes its min-plus product of depth S, and streams back.
+ *   h, n, ld, inf   the matrix, in place in host memory, with the contract
+ *                   of apsp_fw_i32 / apsp_fw_f32 (element (i,j) at h[i*ld+j]).
+ *                   Allocate it pinned (hipHostMalloc) for copies that
+ *                   overlap the products; pageable memory works, slower.
+ *   device_bytes    device memory the call may use (0: half of the free
+ *                   memory); about 4 (2 S n + 4 S^2) bytes are taken.  A
+ *                   budget too small for S = 128 returns APSP_ERR_RANGE.
+ *   outer_block     optional output (may be NULL): the S used.
+ * int32 matrices compute in binary32 when that is exact, as for apsp_fw_i32
+ * (the arithmetic policy applies), decided by a device scan streamed over
+ * the matrix first.  Results equal apsp_fw_i32 / apsp_fw_f32 on the same
+ * matrix (int32 exactly).  Synchronous: returns after all work, on `stream`
+ * and on three internal streams of default priority, has completed.
+ * Errors as for apsp_fw_i32.
+ */
+int apsp_fw_host_i32(int32_t *h, int64_t n, int64_t ld, int32_t inf, int64_t device_bytes,
+                     void *stream, int64_t *outer_block);
+int apsp_fw_host_f32(float *h, int64_t n, int64_t ld, float inf, int64_t device_bytes,
+                     void *stream, int64_t *outer_block);
+
+/*
  * Measurement across calls: after apsp_trace_begin(max_launches), every
  * apsp_fw_i32 / apsp_fw_f32 / apsp_fw_rounds_* call made by this thread
  * records HIP events around each launch (or launch group, as for

@@ -15,6 +15,7 @@ Functions mirror the C library:
     listed source over a CSR graph (negative weights allowed);
   * ``johnson_potentials(row_ptr, col, w, n)``: Johnson's h from an added
     vertex with 0-weight edges to every vertex (Bellman-Ford);
+  * ``minplus(c, a, b, inf)``: the min-plus product min(c, a (x) b);
   * ``apsp(m, inf)``: the full distance matrix of an int32 or float32 input
     (float32 is widened exactly to binary64 and the result stays binary64).
 """
@@ -63,6 +64,10 @@ def load(path: str = LIB):
     lib.oracle_sssp_bf_csr_i64.restype = ctypes.c_int
     lib.oracle_sssp_bf_rows_i64.argtypes = [p, p, p, i64, p, i64, p, i64, p]
     lib.oracle_sssp_bf_rows_i64.restype = ctypes.c_int
+    lib.oracle_minplus_i64.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, i64]
+    lib.oracle_minplus_i64.restype = None
+    lib.oracle_minplus_f64.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64]
+    lib.oracle_minplus_f64.restype = None
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -190,6 +195,30 @@ class Oracle:
         ext_w = np.concatenate([np.asarray(w, dtype=np.int64), np.zeros(n, dtype=np.int64)])
         rows, neg = self.bf_rows_csr(ext_rp, ext_col, ext_w, n + 1, [n], inf=0)
         return rows[0, :n].copy(), bool(neg[0])
+
+    def minplus(self, c, a, b, inf=None):
+        """min(c, a (x) b) as a new array.  Integer inputs: int64 arithmetic,
+        entries equal to inf are "no path" (never summed).  Float inputs:
+        binary64 (+inf sums to +inf by itself)."""
+        if np.issubdtype(np.asarray(c).dtype, np.integer):
+            cc = np.array(c, dtype=np.int64, order="C", copy=True)
+            aa = np.ascontiguousarray(a, dtype=np.int64)
+            bb = np.ascontiguousarray(b, dtype=np.int64)
+            m, n = cc.shape
+            k = aa.shape[1]
+            if m and n and k:
+                self.lib.oracle_minplus_i64(cc.ctypes.data, n, aa.ctypes.data, k, bb.ctypes.data,
+                                            n, m, n, k, int(inf))
+            return cc
+        cc = np.array(c, dtype=np.float64, order="C", copy=True)
+        aa = np.ascontiguousarray(a, dtype=np.float64)
+        bb = np.ascontiguousarray(b, dtype=np.float64)
+        m, n = cc.shape
+        k = aa.shape[1]
+        if m and n and k:
+            self.lib.oracle_minplus_f64(cc.ctypes.data, n, aa.ctypes.data, k, bb.ctypes.data, n,
+                                        m, n, k)
+        return cc
 
     def apsp(self, m: np.ndarray) -> np.ndarray:
         """Full distance matrix: int32 stays int32, float32 becomes float64."""

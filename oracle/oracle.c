@@ -293,3 +293,43 @@ int oracle_sssp_bf_rows_i64(const int64_t *row_ptr, const int32_t *col, const in
   }
   return bad ? -1 : 0;
 }
+
+/*
+ * Min-plus product C <- min(C, A (x) B), (A (x) B)[i][j] = min over t of
+ * A[i][t] + B[t][j]: the update of a block from its pivot-row and
+ * pivot-column blocks on the "Katz and Kider" page (thesis section 4.6,
+ * Algorithms 17-18), written as the definition.  Entries equal to inf are
+ * "no path": a candidate through one is not formed.  int64 (exact) and
+ * binary64 (single IEEE additions, exact min) versions; OpenMP over rows.
+ */
+void oracle_minplus_i64(int64_t *c, int64_t ldc, const int64_t *a, int64_t lda,
+                        const int64_t *b, int64_t ldb, int64_t m, int64_t n, int64_t k,
+                        int64_t inf) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t t = 0; t < k; ++t) {
+      const int64_t ait = a[i * lda + t];
+      if (ait == inf) continue;
+      for (int64_t j = 0; j < n; ++j) {
+        const int64_t btj = b[t * ldb + j];
+        if (btj == inf) continue;
+        const int64_t cand = ait + btj;
+        if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;
+      }
+    }
+}
+
+void oracle_minplus_f64(double *c, int64_t ldc, const double *a, int64_t lda, const double *b,
+                        int64_t ldb, int64_t m, int64_t n, int64_t k) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t t = 0; t < k; ++t) {
+      const double ait = a[i * lda + t];
+      for (int64_t j = 0; j < n; ++j) {
+        const double cand = ait + b[t * ldb + j];
+        if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;
+      }
+    }
+}

@@ -197,3 +197,39 @@ def test_trace_argument_errors(lib):
     assert ga.apsp_trace_begin((1 << 24) + 1) == ga.APSP_ERR_INVALID_VALUE
     st, ms, cnt, dropped = ga.apsp_trace_end()        # none is on
     assert st == ga.APSP_ERR_INVALID_VALUE and cnt == [0, 0, 0, 0] and dropped == 0
+
+
+@pytest.mark.parametrize("args", [
+    # C, ldc, A, lda, B, ldb, m, n, k, inf
+    (FAKE, 8, FAKE, 8, FAKE, 8, -1, 8, 8, 100),       # m < 0
+    (FAKE, 8, FAKE, 8, FAKE, 8, 8, 8, -1, 100),       # k < 0
+    (0, 8, FAKE, 8, FAKE, 8, 8, 8, 8, 100),           # null C
+    (FAKE, 8, 0, 8, FAKE, 8, 8, 8, 8, 100),           # null A
+    (FAKE, 8, FAKE, 8, 0, 8, 8, 8, 8, 100),           # null B
+    (FAKE, 7, FAKE, 8, FAKE, 8, 8, 8, 8, 100),        # ldc < n
+    (FAKE, 8, FAKE, 7, FAKE, 8, 8, 8, 8, 100),        # lda < k
+    (FAKE, 8, FAKE, 8, FAKE, 7, 8, 8, 8, 100),        # ldb < n
+    (FAKE + 2, 8, FAKE, 8, FAKE, 8, 8, 8, 8, 100),    # misaligned
+    (FAKE, 8, FAKE, 8, FAKE, 8, 8, 8, 8, 0),          # bad inf
+    (FAKE, 8, FAKE, 8, FAKE, 8, 8, 8, 8, 0x40000000),
+])
+def test_gemm_argument_errors(lib, args):
+    assert ga.apsp_minplus_gemm_i32(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_gemm_empty_is_a_no_op_and_f32_inf(lib):
+    assert ga.apsp_minplus_gemm_i32(0, 1, 0, 1, 0, 1, 0, 5, 5, 100, 0) == ga.APSP_OK
+    assert ga.apsp_minplus_gemm_f32(0, 1, 0, 1, 0, 1, 5, 5, 0, 1.0, 0) == ga.APSP_OK
+    for inf in (0.0, -1.0, float("nan")):
+        assert ga.apsp_minplus_gemm_f32(FAKE, 8, FAKE, 8, FAKE, 8, 8, 8, 8, inf, 0) == \
+            ga.APSP_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("args", [
+    (FAKE, -1, 4, 100, 0), (0, 4, 4, 100, 0), (FAKE, 8, 7, 100, 0), (FAKE + 2, 4, 4, 100, 0),
+    (FAKE, 4, 4, 0, 0), (FAKE, 4, 4, 100, -1),
+])
+def test_host_argument_errors(lib, args):
+    st, blk = ga.apsp_fw_host_i32(*args)
+    assert st == ga.APSP_ERR_INVALID_VALUE and blk == 0
+    assert ga.apsp_fw_host_i32(0, 0, 1, 100)[0] == ga.APSP_OK

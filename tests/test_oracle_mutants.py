@@ -59,6 +59,14 @@ MUTANTS = {
     "bf_cycle_never": ("    if (!changed) return 0;\n  }\n  return 1;",
                        "    if (!changed) return 0;\n  }\n  return 0;"),
     "bf_edge_target_is_source": ("const int64_t v = col[e];", "const int64_t v = u;"),
+    # min-plus product
+    "mp_transposed_b": ("const int64_t btj = b[t * ldb + j];", "const int64_t btj = b[j * ldb + t];"),
+    "mp_ignores_c": ("        if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;\n      }\n    }\n}\n\nvoid oracle_minplus_f64",
+                     "        if (cand < c[i * ldc + j] || t == 0) c[i * ldc + j] = cand;\n      }\n    }\n}\n\nvoid oracle_minplus_f64"),
+    "mp_last_t_skipped": ("    for (int64_t t = 0; t < k; ++t) {\n      const int64_t ait",
+                          "    for (int64_t t = 0; t < k - 1; ++t) {\n      const int64_t ait"),
+    "mp_guard_dropped": ("      if (ait == inf) continue;\n      for (int64_t j = 0; j < n; ++j) {\n        const int64_t btj",
+                         "      for (int64_t j = 0; j < n; ++j) {\n        const int64_t btj"),
 }
 
 
@@ -144,6 +152,25 @@ def _battery_bellman_ford(o: oracle.Oracle) -> None:
         assert np.array_equal(got, brute_force_apsp(w, INF).astype(np.int64))
 
 
+def _battery_minplus(o: oracle.Oracle) -> None:
+    a = np.array([[0, 4, INF], [2, INF, 1]], dtype=np.int64)
+    b = np.array([[5, INF], [0, 3], [7, 1]], dtype=np.int64)
+    c = np.array([[3, 2], [INF, INF]], dtype=np.int64)
+    assert o.minplus(c, a, b, INF).tolist() == [[3, 2], [7, 2]]
+    # a "no path" operand is never summed, even next to a negative entry
+    neg = o.minplus(np.array([[INF]], dtype=np.int64), np.array([[INF]], dtype=np.int64),
+                    np.array([[-5]], dtype=np.int64), INF)
+    assert neg.tolist() == [[INF]]
+    rng = np.random.default_rng(11)
+    for _ in range(4):
+        n = int(rng.integers(3, 40))
+        w = random_small_graph(rng, n, 0.15, 30, INF)
+        d = w.astype(np.int64)
+        for _ in range(int(np.ceil(np.log2(n - 1))) if n > 2 else 1):
+            d = o.minplus(d, d, d.copy(), INF)
+        assert np.array_equal(d, o.fw_i32(w).astype(np.int64))
+
+
 def _build_variant(tmp_path, name, edit):
     src = open(oracle.SRC).read()
     if edit is not None:
@@ -162,6 +189,7 @@ def test_battery_passes_on_unmodified_oracle(tmp_path):
     _battery(o)
     _battery_guarded(o)
     _battery_bellman_ford(o)
+    _battery_minplus(o)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -171,3 +199,4 @@ def test_battery_catches_mutant(tmp_path, name):
         _battery(o)
         _battery_guarded(o)
         _battery_bellman_ford(o)
+        _battery_minplus(o)

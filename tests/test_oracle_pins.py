@@ -424,3 +424,65 @@ def test_float_fw_with_ieee_inf_handles_negative_weights(orc, seed):
     assert np.array_equal(np.isinf(got), np.isinf(want))
     fin = np.isfinite(want)
     assert np.allclose(got[fin], want[fin], rtol=1e-12, atol=1e-12)
+
+
+# ---- the min-plus product ---------------------------------------------------
+
+def test_minplus_hand_example(orc):
+    # worked by hand: a 2 x 3 by 3 x 2 product, one "no path" entry, C keeps
+    # an entry the product cannot beat
+    a = np.array([[0, 4, INF], [2, INF, 1]], dtype=np.int64)
+    b = np.array([[5, INF], [0, 3], [7, 1]], dtype=np.int64)
+    c = np.array([[3, 2], [INF, INF]], dtype=np.int64)
+    got = orc.minplus(c, a, b, INF)
+    # (0,0): min(3, 0+5, 4+0) = 3; (0,1): min(2, 4+3) = 2
+    # (1,0): min(2+5, 1+7) = 7;    (1,1): min(1+1) = 2
+    assert got.tolist() == [[3, 2], [7, 2]]
+    # a "no path" operand is never summed, even next to a negative entry:
+    # inf + (-5) must not beat inf
+    one = lambda v: np.array([[v]], dtype=np.int64)
+    assert orc.minplus(one(INF), one(INF), one(-5), INF).tolist() == [[INF]]
+    assert orc.minplus(one(INF), one(-5), one(INF), INF).tolist() == [[INF]]
+    assert orc.minplus(one(INF), one(-5), one(2), INF).tolist() == [[-3]]
+
+
+def test_minplus_identity_and_associativity(orc):
+    rng = np.random.default_rng(7)
+    n = 30
+    ident = np.full((n, n), INF, dtype=np.int64)
+    np.fill_diagonal(ident, 0)
+    empty = np.full((n, n), INF, dtype=np.int64)
+    for trial in range(10):
+        a = random_small_graph(rng, n, 0.3, 50, INF).astype(np.int64)
+        b = random_small_graph(rng, n, 0.3, 50, INF).astype(np.int64)
+        d = random_small_graph(rng, n, 0.3, 50, INF).astype(np.int64)
+        assert np.array_equal(orc.minplus(empty, a, ident, INF), a)
+        assert np.array_equal(orc.minplus(empty, ident, a, INF), a)
+        ab = orc.minplus(empty, a, b, INF)
+        bd = orc.minplus(empty, b, d, INF)
+        assert np.array_equal(orc.minplus(empty, ab, d, INF), orc.minplus(empty, a, bd, INF))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_minplus_squaring_reaches_the_floyd_warshall_closure(orc, seed):
+    # W with a zero diagonal: W^(2^r) covers paths of up to 2^r edges, so
+    # ceil(log2(n - 1)) squarings give delta, which the pinned plain
+    # recurrence computes by another route
+    rng = np.random.default_rng(900 + seed)
+    n = int(rng.integers(2, 70))
+    w = random_small_graph(rng, n, [0.05, 0.2][seed % 2], 30, INF)
+    d = w.astype(np.int64)
+    for _ in range(max(1, int(np.ceil(np.log2(max(n - 1, 2)))))):
+        d = orc.minplus(d, d, d.copy(), INF)
+    assert np.array_equal(d, orc.fw_i32(w).astype(np.int64))
+
+
+def test_minplus_float_with_ieee_inf(orc):
+    rng = np.random.default_rng(8)
+    m, n, k = 20, 25, 30
+    a = np.where(rng.random((m, k)) < 0.5, rng.uniform(0.01, 1.0, (m, k)), np.inf)
+    b = np.where(rng.random((k, n)) < 0.5, rng.uniform(0.01, 1.0, (k, n)), np.inf)
+    c = np.full((m, n), np.inf)
+    got = orc.minplus(c, a, b)
+    want = np.min(a[:, :, None] + b[None, :, :], axis=1)   # every candidate at once
+    assert np.array_equal(got, want)
