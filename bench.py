@@ -519,6 +519,75 @@ def bench_host(args) -> int:
     return 0
 
 
+def bench_paths(args) -> int:
+    """Distances plus successors: a step is one apsp_fw_i32 call and one
+    apsp_successors_i32 call on the complete-8192 workload; the roofline entry
+    is the successor kernel (one launch per step, HIP events on its stream)."""
+    import numpy as np
+    import torch
+
+    import graph_all_pairs_amd as ga
+    import graphgen as gg
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = args.workload[len("paths-"):]
+    w = gg.make_workload(base)
+    n = w.shape[0]
+    sha = gg.sha256_matrix(w, n)
+    log(f"workload {args.workload}: successors of {base}, n={n}")
+    tw = torch.from_numpy(w).to(dev)
+    copies = [tw.clone() for _ in range(args.warmup + args.steps)]
+    nxt = torch.empty((n, n), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def step(d, evs=None):
+        if ga.apsp_fw_i32(d.data_ptr(), n, n, gg.INF_I32, s) != ga.APSP_OK:
+            raise RuntimeError("apsp_fw_i32 failed")
+        if evs:
+            evs[0].record(stream)
+        if ga.apsp_successors_i32(tw.data_ptr(), n, d.data_ptr(), n, nxt.data_ptr(), n, n,
+                                  gg.INF_I32, s) != ga.APSP_OK:
+            raise RuntimeError("apsp_successors_i32 failed")
+        if evs:
+            evs[1].record(stream)
+
+    for i in range(args.warmup):
+        step(copies[i])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(copies[args.warmup + i], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    succ_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms_per_step = 1e3 * wall / args.steps
+    # 4 int32 VALU instructions per candidate (add, compare, two selects)
+    peak = VALU_LANE_OPS["int32"] / 4
+    achieved = float(n) ** 3 / (succ_ms * 1e-3)
+    log(f"timed {args.steps} steps: {ms_per_step:.1f} ms/step, successor kernel {succ_ms:.2f} ms")
+    rec = {
+        "metric": "APSP distances plus successor matrix, n^3/time",
+        "value": float(n) ** 3 / (wall / args.steps),
+        "unit": "relaxations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n, "input_sha256": sha,
+                   "successor_ms": succ_ms, "fw_ms": ms_per_step - succ_ms},
+        "roofline": {"bound": "alu", "kernel": "successors", "achieved": achieved / 1e12,
+                     "peak": peak / 1e12, "unit": "Tcandidates/s", "frac": achieved / peak,
+                     "traffic": None, "avg_launch_ms": succ_ms, "launches": args.steps,
+                     "note": "peak: int32 VALU rate / 4 instructions per candidate"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +619,8 @@ def main() -> int:
         return bench_johnson(args)
     if args.workload in gg.HOST_WORKLOADS:
         return bench_host(args)
+    if args.workload.startswith("paths-") and args.workload[len("paths-"):] in gg.WORKLOADS:
+        return bench_paths(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

@@ -60,7 +60,8 @@ EXPORTS = (
     "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
     "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
     "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
-    "apsp_fw_host_i32", "apsp_fw_host_f32",
+    "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_successors_i32", "apsp_successors_f32",
+    "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
 )
 
 _lib = None
@@ -120,6 +121,11 @@ def load(path: str | None = None):
         "apsp_minplus_gemm_f32": ([vp, i64, vp, i64, vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
         "apsp_fw_host_i32": ([vp, i64, i64, i32, i64, vp, lp], ctypes.c_int),
         "apsp_fw_host_f32": ([vp, i64, i64, f32, i64, vp, lp], ctypes.c_int),
+        "apsp_successors_i32": ([vp, i64, vp, i64, vp, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_successors_f32": ([vp, i64, vp, i64, vp, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_fw_paths_i32": ([vp, i64, vp, i64, i64, i32, vp], ctypes.c_int),
+        "apsp_fw_paths_f32": ([vp, i64, vp, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_path": ([vp, i64, i64, i64, i64, vp, i64], i64),
         "apsp_trace_begin": ([i64], ctypes.c_int),
         "apsp_trace_end": ([dp, lp, lp], ctypes.c_int),
         "apsp_fw_signed_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
@@ -193,6 +199,28 @@ def apsp_fw_host_f32(h_ptr, n, ld, inf, device_bytes=0, stream=0):
     st = load().apsp_fw_host_f32(h_ptr or None, n, ld, inf, device_bytes, stream or None,
                                  ctypes.byref(blk))
     return int(st), int(blk.value)
+
+
+def apsp_successors_i32(w, ldw, d, ldd, nxt, ldn, n, inf, stream=0) -> int:
+    return load().apsp_successors_i32(w or None, ldw, d or None, ldd, nxt or None, ldn, n, inf,
+                                      stream or None)
+
+
+def apsp_successors_f32(w, ldw, d, ldd, nxt, ldn, n, inf, stream=0) -> int:
+    return load().apsp_successors_f32(w or None, ldw, d or None, ldd, nxt or None, ldn, n, inf,
+                                      stream or None)
+
+
+def apsp_fw_paths_i32(d, ld, nxt, ldn, n, inf, stream=0) -> int:
+    return load().apsp_fw_paths_i32(d or None, ld, nxt or None, ldn, n, inf, stream or None)
+
+
+def apsp_fw_paths_f32(d, ld, nxt, ldn, n, inf, stream=0) -> int:
+    return load().apsp_fw_paths_f32(d or None, ld, nxt or None, ldn, n, inf, stream or None)
+
+
+def apsp_path(nxt_host_ptr, ldn, n, i, j, path_ptr=0, cap=0) -> int:
+    return int(load().apsp_path(nxt_host_ptr or None, ldn, n, i, j, path_ptr or None, cap))
 
 
 def apsp_trace_begin(max_launches: int) -> int:
@@ -482,3 +510,37 @@ def fw_host(t, inf=None, device_bytes=0):
     if st != APSP_OK:
         _raise(st, "apsp_fw_host")
     return blk
+
+
+def fw_paths(t, nxt=None, inf=None):
+    """In-place APSP of t[:n, :n] plus the successor matrix (int32 (n, n)
+    CUDA tensor, allocated when None); returns nxt."""
+    import torch
+    kind, p, n, ld, inf, s = _tensor_args(t, inf)
+    if nxt is None:
+        nxt = torch.empty((n, n), dtype=torch.int32, device=t.device)
+    if nxt.dtype != torch.int32 or nxt.dim() != 2 or nxt.shape[0] != n or nxt.shape[1] < n:
+        raise ValueError("nxt must be an int32 (n, >= n) tensor")
+    ldn = nxt.stride(0) if n > 1 else max(nxt.shape[1], 1)
+    with torch.cuda.device(t.device):
+        st = (apsp_fw_paths_i32 if kind == "i32" else apsp_fw_paths_f32)(p, ld, nxt.data_ptr(),
+                                                                         ldn, n, inf, s)
+    if st != APSP_OK:
+        _raise(st, "apsp_fw_paths_" + kind)
+    return nxt
+
+
+def path(nxt_host, i, j):
+    """Vertices of the path i -> j from a successor matrix in host memory (a
+    contiguous int32 numpy array): a list, [] when unreachable.  Raises on a
+    successor cycle."""
+    import numpy as np
+    a = np.ascontiguousarray(nxt_host, dtype=np.int32)
+    n, ldn = a.shape[0], a.shape[1]
+    buf = np.empty(n + 1, dtype=np.int32)
+    r = apsp_path(a.ctypes.data, ldn, n, i, j, buf.ctypes.data, len(buf))
+    if r == -1:
+        return []
+    if r < 0:
+        raise ValueError(f"apsp_path failed ({r})")
+    return buf[:r].tolist()

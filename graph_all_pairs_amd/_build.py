@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "apsp.hip")
-SOURCES = [SRC] + [os.path.join(PKG, "csrc", f) for f in ("batched.hip", "ceiling.hip", "johnson.hip", "gemm.hip", "host.hip")]
+SOURCES = [SRC] + [os.path.join(PKG, "csrc", f) for f in ("batched.hip", "ceiling.hip", "johnson.hip", "gemm.hip", "host.hip", "paths.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libapsp.so")
 ARCH = "gfx950"

@@ -1,0 +1,289 @@
+// Path reconstruction: the successor (first-hop) matrix of all-pairs
+// shortest paths, from the weights and the final distances.
+//
+// For i != j, nxt[i][j] is the smallest vertex u != i that minimises
+// w(i, u) + d(u, j) -- the first hop of a shortest path, by Bellman's
+// equation d(i, j) = min over u != i of w(i, u) + d(u, j) (a shortest path
+// from i leaves i through some first edge).  nxt[i][i] = i, and -1 where j is
+// unreachable from i.  This is the relaxation RelaxEdge of the page
+// "Johnson's APSP in Glushkov algorithmic algebras" applied once more to the
+// final distances, keeping the argument of the minimum; the result does not
+// depend on the order in which the blocked rounds found the distances, so it
+// is unique.  Following nxt from i reaches j along a path of total weight
+// d(i, j) when every weight is positive (each hop lowers the remaining
+// distance).
+//
+// gfx950 design: the min-plus product W (x) D of the product kernel
+// (gemm.hip) with the minimum's argument tracked: a 256-thread workgroup owns
+// a 128 x 128 tile of (value, index) pairs as 8 x 8 micro-tiles in
+// registers, W's rows and D's rows stream through LDS in 16-deep chunks
+// (double buffered), u runs in increasing order and a candidate replaces the
+// pair only when strictly smaller, so the smallest u wins ties.  W[i][i] is
+// staged as inf (u != i).  Per candidate: add, compare, two selects.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "apsp.h"
+#include "detail.h"
+#include "minplus.h"
+
+namespace {
+
+using namespace apsp_dev;
+
+constexpr int kT = 128;
+constexpr int kThreads = 256;
+constexpr int kR = 8;
+constexpr int kThr = kT / kR;
+constexpr int kKC = 16;
+constexpr int kLd = kT + 4;
+constexpr int kGroupStride = kT / (kR / 4);
+constexpr int kLoads = kT * kKC / 4 / kThreads;
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void ld4(const T* __restrict__ p, int64_t ld, int64_t rows, int64_t cols,
+                                    int64_t r, int64_t c, T inf, T (&v)[4]) {
+  const T* q = p + r * ld + c;
+  if (r < rows && c + 3 < cols) {
+    if (VEC) {
+      load4(q, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = q[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (r < rows && c + e < cols) ? q[e] : inf;
+  }
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_t ldd,
+           int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf, uint32_t tiles_per_row) {
+  __shared__ __attribute__((aligned(16))) T lds[4 * kKC * kLd];
+  T* sA = lds;                  // [2][kKC][kLd]: sA[t][row] = W[row0 + row][u0 + t]
+  T* sB = lds + 2 * kKC * kLd;  // [2][kKC][kLd]: sB[t][col] = D[u0 + t][col0 + col]
+  const int tid = threadIdx.x;
+  const int tc = tid % kThr, tr = tid / kThr;
+  const int64_t row0 = (int64_t)(blockIdx.x / tiles_per_row) * kT;
+  const int64_t col0 = (int64_t)(blockIdx.x % tiles_per_row) * kT;
+
+  T val[kR][kR];
+  int32_t idx[kR][kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i)
+#pragma unroll
+    for (int j = 0; j < kR; ++j) {
+      val[i][j] = inf;
+      idx[i][j] = -1;
+    }
+
+  T ga[kLoads][4], gb[kLoads][4];
+  auto fetch = [&](int64_t u0) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int q = tid + l * kThreads;
+      const int r = q / (kKC / 4), uq = q % (kKC / 4);
+      ld4<T, VEC>(W, ldw, n, n, row0 + r, u0 + uq * 4, inf, ga[l]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)  // u != i: the vertex itself is never its own first hop
+        if (row0 + r == u0 + uq * 4 + e) ga[l][e] = inf;
+      const int ur = q / (kT / 4), cq = q % (kT / 4);
+      ld4<T, VEC>(D, ldd, n, n, u0 + ur, col0 + cq * 4, inf, gb[l]);
+    }
+  };
+  auto stash = [&](int buf) {
+    T* a = sA + buf * kKC * kLd;
+    T* b = sB + buf * kKC * kLd;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int q = tid + l * kThreads;
+      const int r = q / (kKC / 4), uq = q % (kKC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[(uq * 4 + e) * kLd + r] = ga[l][e];
+      const int ur = q / (kT / 4), cq = q % (kT / 4);
+      store4(b + ur * kLd + cq * 4, gb[l]);
+    }
+  };
+
+  const int64_t chunks = (n + kKC - 1) / kKC;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int64_t c = 0; c < chunks; ++c) {
+    const int buf = (int)(c & 1);
+    if (c + 1 < chunks) fetch((c + 1) * kKC);
+    const T* a = sA + buf * kKC * kLd;
+    const T* b = sB + buf * kKC * kLd;
+    const int32_t u0 = (int32_t)(c * kKC);
+#pragma unroll 2
+    for (int t = 0; t < kKC; ++t) {
+      T av[kR], bv[kR];
+#pragma unroll
+      for (int gi = 0; gi < kR / 4; ++gi) {
+        T v[4];
+        load4(a + t * kLd + gi * kGroupStride + tr * 4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[gi * 4 + i] = v[i];
+        load4(b + t * kLd + gi * kGroupStride + tc * 4, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[gi * 4 + j] = v[j];
+      }
+      const int32_t u = u0 + t;
+#pragma unroll
+      for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int j = 0; j < kR; ++j) {
+          const T cand = av[i] + bv[j];
+          const bool better = cand < val[i][j];
+          val[i][j] = better ? cand : val[i][j];
+          idx[i][j] = better ? u : idx[i][j];
+        }
+    }
+    if (c + 1 < chunks) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int gi = 0; gi < kR / 4; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = row0 + gi * kGroupStride + tr * 4 + i;
+      if (r >= n) continue;
+#pragma unroll
+      for (int gj = 0; gj < kR / 4; ++gj)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = col0 + gj * kGroupStride + tc * 4 + j;
+          if (col >= n) continue;
+          // unreachable: no candidate below inf
+          const int32_t s = r == col ? (int32_t)r : (val[gi * 4 + i][gj * 4 + j] < inf ? idx[gi * 4 + i][gj * 4 + j] : -1);
+          nxt[r * ldn + col] = s;
+        }
+    }
+}
+
+template <typename T>
+bool inf_ok(T inf);
+template <>
+bool inf_ok<int32_t>(int32_t inf) { return inf >= 1 && inf <= 0x3FFFFFFF; }
+template <>
+bool inf_ok<float>(float inf) { return inf > 0.0f; }
+
+template <typename T>
+bool mat_ok(const void* p, int64_t n, int64_t ld, size_t elem) {
+  return p != nullptr && ld >= n && reinterpret_cast<uintptr_t>(p) % elem == 0 &&
+         ld <= INT64_MAX / (int64_t)elem / n;
+}
+
+template <typename T>
+int run_successors(const T* w, int64_t ldw, const T* d, int64_t ldd, int32_t* nxt, int64_t ldn,
+                   int64_t n, T inf, void* stream) {
+  if (n < 0 || !inf_ok<T>(inf)) return APSP_ERR_INVALID_VALUE;
+  if (n == 0) return APSP_OK;
+  if (n >= (int64_t(1) << 31) || !mat_ok<T>(w, n, ldw, sizeof(T)) ||
+      !mat_ok<T>(d, n, ldd, sizeof(T)) || !mat_ok<int32_t>(nxt, n, ldn, sizeof(int32_t)))
+    return APSP_ERR_INVALID_VALUE;
+  const int64_t tpr = (n + kT - 1) / kT;
+  if (tpr * tpr > (int64_t(1) << 31)) return APSP_ERR_INVALID_VALUE;
+  int st = apsp_detail_check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool vec = al16(w) && al16(d) && ldw % 4 == 0 && ldd % 4 == 0;
+  const dim3 grid((unsigned)(tpr * tpr));
+  if (vec)
+    hipLaunchKernelGGL((successors<T, true>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt, ldn,
+                       n, inf, (uint32_t)tpr);
+  else
+    hipLaunchKernelGGL((successors<T, false>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt,
+                       ldn, n, inf, (uint32_t)tpr);
+  return apsp_detail_launch_status();
+}
+
+}  // namespace
+
+extern "C" int apsp_fw_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream);
+extern "C" int apsp_fw_f32(float* d, int64_t n, int64_t ld, float inf, void* stream);
+
+namespace {
+
+// Distances in place plus successors: the weights are kept in
+// stream-ordered scratch for the successor pass.
+template <typename T>
+int run_fw_paths(T* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n, T inf, void* stream) {
+  if (n < 0 || !inf_ok<T>(inf)) return APSP_ERR_INVALID_VALUE;
+  if (n == 0) return APSP_OK;
+  if (!mat_ok<T>(d, n, ld, sizeof(T)) || !mat_ok<int32_t>(nxt, n, ldn, sizeof(int32_t)) ||
+      n >= (int64_t(1) << 31))
+    return APSP_ERR_INVALID_VALUE;
+  int st = apsp_detail_check_device();
+  if (st != APSP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t ldw = (n + 3) & ~int64_t(3);
+  T* w = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&w), (size_t)(ldw * n * sizeof(T)), s) != hipSuccess) {
+    (void)apsp_detail_launch_status();
+    return APSP_ERR_LAUNCH;
+  }
+  if (hipMemcpy2DAsync(w, ldw * sizeof(T), d, ld * sizeof(T), n * sizeof(T), n,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess) {
+    (void)apsp_detail_launch_status();
+    (void)hipFreeAsync(w, s);
+    return APSP_ERR_LAUNCH;
+  }
+  if constexpr (std::is_same_v<T, int32_t>) st = apsp_fw_i32(d, n, ld, inf, stream);
+  else st = apsp_fw_f32(d, n, ld, inf, stream);
+  if (st == APSP_OK) st = run_successors<T>(w, ldw, d, ld, nxt, ldn, n, inf, stream);
+  (void)hipFreeAsync(w, s);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int apsp_fw_paths_i32(int32_t* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n, int32_t inf,
+                      void* stream) {
+  return run_fw_paths<int32_t>(d, ld, nxt, ldn, n, inf, stream);
+}
+
+int apsp_fw_paths_f32(float* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n, float inf,
+                      void* stream) {
+  return run_fw_paths<float>(d, ld, nxt, ldn, n, inf, stream);
+}
+
+
+int apsp_successors_i32(const int32_t* w, int64_t ldw, const int32_t* d, int64_t ldd,
+                        int32_t* nxt, int64_t ldn, int64_t n, int32_t inf, void* stream) {
+  return run_successors<int32_t>(w, ldw, d, ldd, nxt, ldn, n, inf, stream);
+}
+
+int apsp_successors_f32(const float* w, int64_t ldw, const float* d, int64_t ldd, int32_t* nxt,
+                        int64_t ldn, int64_t n, float inf, void* stream) {
+  return run_successors<float>(w, ldw, d, ldd, nxt, ldn, n, inf, stream);
+}
+
+int64_t apsp_path(const int32_t* nxt, int64_t ldn, int64_t n, int64_t i, int64_t j, int32_t* path,
+                  int64_t cap) {
+  if (nxt == nullptr || n <= 0 || ldn < n || i < 0 || i >= n || j < 0 || j >= n || cap < 0 ||
+      (cap > 0 && path == nullptr))
+    return -2;
+  if (nxt[i * ldn + j] < 0) return -1;  // j unreachable from i
+  int64_t len = 0, v = i;
+  for (;;) {
+    if (len < cap) path[len] = (int32_t)v;
+    ++len;
+    if (v == j) return len;
+    if (len > n) return -3;  // no progress within n hops: a zero-weight cycle
+    const int32_t u = nxt[v * ldn + j];
+    if (u < 0 || u >= n) return -3;
+    v = u;
+  }
+}
+
+}  // extern "C"

@@ -202,6 +202,50 @@ int apsp_fw_host_f32(float *h, int64_t n, int64_t ld, float inf, int64_t device_
                      void *stream, int64_t *outer_block);
 
 /*
+ * Path reconstruction: the successor (first-hop) matrix.  For i != j,
+ * nxt[i][j] = the smallest u != i minimising w[i][u] + d[u][j] (a first hop
+ * of a shortest path i -> j, by Bellman's equation d(i,j) = min over u != i
+ * of w(i,u) + d(u,j)); nxt[i][i] = i; -1 where no candidate is below inf (j
+ * unreachable).  It is the page "Johnson's APSP in Glushkov algorithmic
+ * algebras" relaxation RelaxEdge(i, u, j) taken once more over the final
+ * distances, keeping the argument of the minimum, so it does not depend on
+ * the order in which the distances were found.
+ *   w, ldw   device, the n x n weights (as given to apsp_fw_*: w[i][i] = 0,
+ *            inf for "no edge"; int32 entries in [0, inf]);
+ *   d, ldd   device, the n x n shortest distances of w (e.g. apsp_fw_*'s
+ *            output);
+ *   nxt, ldn device int32 output, n x n, ldn >= n.
+ * Pointers 4-byte aligned (128-bit loads when w and d are 16-byte aligned and
+ * ldw, ldd are multiples of 4).  Following nxt from i reaches j along a path
+ * whose weights sum to d[i][j] when every weight on it is positive.
+ * Asynchronous on `stream`; allocates nothing.  Errors as for apsp_fw_i32.
+ */
+int apsp_successors_i32(const int32_t *w, int64_t ldw, const int32_t *d, int64_t ldd,
+                        int32_t *nxt, int64_t ldn, int64_t n, int32_t inf, void *stream);
+int apsp_successors_f32(const float *w, int64_t ldw, const float *d, int64_t ldd, int32_t *nxt,
+                        int64_t ldn, int64_t n, float inf, void *stream);
+
+/*
+ * Distances and successors in one call: apsp_fw_* in place on d, then
+ * apsp_successors_* from a copy of the weights kept in n*n elements of
+ * stream-ordered scratch.  Asynchronous on `stream`.
+ */
+int apsp_fw_paths_i32(int32_t *d, int64_t ld, int32_t *nxt, int64_t ldn, int64_t n, int32_t inf,
+                      void *stream);
+int apsp_fw_paths_f32(float *d, int64_t ld, int32_t *nxt, int64_t ldn, int64_t n, float inf,
+                      void *stream);
+
+/*
+ * The path i -> j from a successor matrix in HOST memory (copy nxt back
+ * first): writes the vertices i, ..., j into path[0 .. min(len, cap)) and
+ * returns len, the number of vertices (1 when i = j).  Returns -1 when j is
+ * unreachable from i, -2 for bad arguments, -3 when the successors do not
+ * reach j within n hops (a zero-weight cycle).  Host code only.
+ */
+int64_t apsp_path(const int32_t *nxt, int64_t ldn, int64_t n, int64_t i, int64_t j,
+                  int32_t *path, int64_t cap);
+
+/*
  * Measurement across calls: after apsp_trace_begin(max_launches), every
  * apsp_fw_i32 / apsp_fw_f32 / apsp_fw_rounds_* call made by this thread
  * records HIP events around each launch (or launch group, as for

@@ -16,6 +16,8 @@ Functions mirror the C library:
   * ``johnson_potentials(row_ptr, col, w, n)``: Johnson's h from an added
     vertex with 0-weight edges to every vertex (Bellman-Ford);
   * ``minplus(c, a, b, inf)``: the min-plus product min(c, a (x) b);
+  * ``successors(w, d, inf)``: the first-hop matrix of weights w and
+    distances d;
   * ``apsp(m, inf)``: the full distance matrix of an int32 or float32 input
     (float32 is widened exactly to binary64 and the result stays binary64).
 """
@@ -68,6 +70,8 @@ def load(path: str = LIB):
     lib.oracle_minplus_i64.restype = None
     lib.oracle_minplus_f64.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64]
     lib.oracle_minplus_f64.restype = None
+    lib.oracle_successors_i64.argtypes = [p, p, p, i64, i64, i64]
+    lib.oracle_successors_i64.restype = None
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -219,6 +223,18 @@ class Oracle:
             self.lib.oracle_minplus_f64(cc.ctypes.data, n, aa.ctypes.data, k, bb.ctypes.data, n,
                                         m, n, k)
         return cc
+
+    def successors(self, w, d, inf):
+        """First-hop matrix (int32) of weights w and distances d (both n x n
+        integer arrays): smallest u != i minimising w[i][u] + d[u][j]."""
+        ww = np.ascontiguousarray(w, dtype=np.int64)
+        dd = np.ascontiguousarray(d, dtype=np.int64)
+        n = ww.shape[0]
+        nxt = np.empty((n, n), dtype=np.int32)
+        if n:
+            self.lib.oracle_successors_i64(ww.ctypes.data, dd.ctypes.data, nxt.ctypes.data, n, n,
+                                           int(inf))
+        return nxt
 
     def apsp(self, m: np.ndarray) -> np.ndarray:
         """Full distance matrix: int32 stays int32, float32 becomes float64."""

@@ -333,3 +333,27 @@ void oracle_minplus_f64(double *c, int64_t ldc, const double *a, int64_t lda, co
       }
     }
 }
+
+/*
+ * Successor (first-hop) matrix, by its definition: for i != j, nxt[i][j] is
+ * the smallest u != i minimising w[i][u] + d[u][j] over the u whose two
+ * terms are both below inf (RelaxEdge of the Johnson's-APSP page over the
+ * final distances, keeping the argument), -1 when there is none; nxt[i][i] =
+ * i.  w and d are n x n int64 (leading dimension ld), nxt int32 (ld).
+ */
+void oracle_successors_i64(const int64_t *w, const int64_t *d, int32_t *nxt, int64_t n, int64_t ld,
+                           int64_t inf) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = 0; j < n; ++j) {
+      if (i == j) { nxt[i * ld + j] = (int32_t)i; continue; }
+      int64_t best = 0, arg = -1;
+      for (int64_t u = 0; u < n; ++u) {
+        if (u == i || w[i * ld + u] == inf || d[u * ld + j] == inf) continue;
+        const int64_t cand = w[i * ld + u] + d[u * ld + j];
+        if (arg < 0 || cand < best) { best = cand; arg = u; }
+      }
+      nxt[i * ld + j] = (int32_t)arg;
+    }
+}

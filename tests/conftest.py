@@ -16,8 +16,8 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def orc():
-    """The CPU oracle (built here only when no build exists yet)."""
+    """The CPU oracle (built here when no build exists yet or the source is newer)."""
     import oracle
-    if not os.path.exists(oracle.LIB):
+    if not os.path.exists(oracle.LIB) or os.path.getmtime(oracle.LIB) < os.path.getmtime(oracle.SRC):
         oracle.build()
     return oracle.default()

@@ -233,3 +233,38 @@ def test_host_argument_errors(lib, args):
     st, blk = ga.apsp_fw_host_i32(*args)
     assert st == ga.APSP_ERR_INVALID_VALUE and blk == 0
     assert ga.apsp_fw_host_i32(0, 0, 1, 100)[0] == ga.APSP_OK
+
+
+def test_path_walker_on_host_memory(lib):
+    import numpy as np
+    # successors of the hand-worked example (tests/golden/hand4_fw.txt)
+    nxt = np.array([[0, 1, 1, 1], [-1, 1, 2, 2], [-1, 3, 2, 3], [-1, 1, 1, 3]], dtype=np.int32)
+    assert ga.path(nxt, 0, 3) == [0, 1, 2, 3]
+    assert ga.path(nxt, 2, 1) == [2, 3, 1]
+    assert ga.path(nxt, 1, 1) == [1]
+    assert ga.path(nxt, 1, 0) == []
+    # too small an output buffer: the length is still returned
+    buf = np.zeros(2, dtype=np.int32)
+    assert ga.apsp_path(nxt.ctypes.data, 4, 4, 0, 3, buf.ctypes.data, 2) == 4
+    assert buf.tolist() == [0, 1]
+    # bad arguments and a successor cycle
+    assert ga.apsp_path(nxt.ctypes.data, 4, 4, 0, 4, 0, 0) == -2
+    assert ga.apsp_path(0, 4, 4, 0, 1, 0, 0) == -2
+    loop = np.array([[0, 1, 1], [0, 1, 0], [-1, -1, 2]], dtype=np.int32)
+    assert ga.apsp_path(loop.ctypes.data, 3, 3, 0, 2, 0, 0) == -3
+    with pytest.raises(ValueError):
+        ga.path(loop, 0, 2)
+
+
+@pytest.mark.parametrize("fn", ["apsp_successors_i32", "apsp_fw_paths_i32"])
+def test_successor_argument_errors(lib, fn):
+    f = getattr(ga, fn)
+    if fn == "apsp_successors_i32":
+        bad = [(FAKE, 4, FAKE, 4, FAKE, 4, -1, 100), (0, 4, FAKE, 4, FAKE, 4, 4, 100),
+               (FAKE, 3, FAKE, 4, FAKE, 4, 4, 100), (FAKE, 4, FAKE, 4, FAKE + 2, 4, 4, 100),
+               (FAKE, 4, FAKE, 4, FAKE, 4, 4, 0)]
+    else:
+        bad = [(FAKE, 4, FAKE, 4, -1, 100), (0, 4, FAKE, 4, 4, 100), (FAKE, 4, FAKE, 3, 4, 100),
+               (FAKE, 4, FAKE, 4, 4, 0x40000000)]
+    for args in bad:
+        assert f(*args, 0) == ga.APSP_ERR_INVALID_VALUE

@@ -1,0 +1,107 @@
+"""GPU parity of path reconstruction: the successor (first-hop) matrix
+(apsp_successors_*, apsp_fw_paths_*) against the oracle's definition --
+for i != j the smallest u != i minimising w[i][u] + d[u][j] -- bit-exact for
+int32, on graphs with many equal-length paths (small integer weights, unit
+grids).  float32 successors are checked for validity: the path they give
+has the shortest distance's weight.
+"""
+import numpy as np
+import torch
+import pytest
+
+import graph_all_pairs_amd as ga
+import graphgen as gg
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+INF = gg.INF_I32
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def gpu_successors(dev, w, d, ldn=None, offset=0):
+    n = w.shape[0]
+    ldn = n if ldn is None else ldn
+    tw = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+    td = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
+    buf = torch.full((n * ldn + offset + 4,), -9, dtype=torch.int32, device=dev)
+    out = buf[offset:offset + n * ldn].view(n, ldn)
+    s = torch.cuda.current_stream().cuda_stream
+    fn = ga.apsp_successors_i32 if w.dtype == np.int32 else ga.apsp_successors_f32
+    inf = INF if w.dtype == np.int32 else float("inf")
+    st = fn(tw.data_ptr(), n, td.data_ptr(), n, out.data_ptr(), ldn, n, inf, s)
+    assert st == ga.APSP_OK, ga.apsp_status_string(st)
+    host = buf.cpu().numpy()
+    full = host[offset:offset + n * ldn].reshape(n, ldn)
+    assert (full[:, n:] == -9).all() and (host[:offset] == -9).all()
+    assert (host[offset + n * ldn:] == -9).all()
+    return full[:, :n].copy()
+
+
+def tie_graph(n, p, seed):
+    w = gg.erdos_renyi(n, p, 1, 3, seed)        # weights 1..3: many equal-length paths
+    return w
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 64, 127, 128, 129, 300, 1000, 1031])
+def test_int32_successors_match_oracle(dev, orc, n):
+    print(f"case successors i32 n={n}", flush=True)
+    w = tie_graph(n, 0.05 if n > 64 else 0.3, 500 + n)
+    d = orc.fw_i32(w)
+    got = gpu_successors(dev, w, d)
+    assert np.array_equal(got, orc.successors(w, d, INF))
+
+
+def test_grid_successors_and_paths(dev, orc):
+    print("case successors grid", flush=True)
+    w = gg.grid(24, 30)
+    d = orc.fw_i32(w)
+    got = gpu_successors(dev, w, d, ldn=w.shape[0] + 5, offset=1)
+    assert np.array_equal(got, orc.successors(w, d, INF))
+    # walking the successors gives a path of the shortest length
+    n = w.shape[0]
+    rng = np.random.default_rng(1)
+    for i, j in rng.integers(0, n, size=(50, 2)):
+        p = ga.path(got, int(i), int(j))
+        assert p[0] == i and p[-1] == j
+        assert sum(int(w[a, b]) for a, b in zip(p, p[1:])) == d[i, j]
+
+
+def test_fw_paths_combined(dev, orc):
+    print("case fw_paths i32 and f32", flush=True)
+    n = 700
+    w = tie_graph(n, 0.01, 77)
+    t = torch.from_numpy(w).to(dev)
+    nxt = ga.fw_paths(t, inf=INF)
+    d = orc.fw_i32(w)
+    assert np.array_equal(t.cpu().numpy(), d)
+    assert np.array_equal(nxt.cpu().numpy(), orc.successors(w, d, INF))
+    # unreachable pairs give -1
+    wf = gg.complete_f32(300, 9)
+    wf[:150, 150:] = np.inf                        # no edge from the first half to the second
+    tf = torch.from_numpy(wf).to(dev)
+    nf = ga.fw_paths(tf).cpu().numpy()
+    df = tf.cpu().numpy()
+    assert (nf[:150, 150:] == -1).all()
+    rng = np.random.default_rng(2)
+    for i, j in rng.integers(0, 300, size=(200, 2)):
+        p = ga.path(nf, int(i), int(j))
+        if not np.isfinite(df[i, j]):
+            assert p == []
+            continue
+        length = sum(float(wf[a, b]) for a, b in zip(p, p[1:]))
+        assert abs(length - float(df[i, j])) <= 1e-5 * max(abs(float(df[i, j])), 1.0)
+
+
+def test_successors_on_the_complete_workload_shape(dev, orc):
+    print("case successors complete n=2048", flush=True)
+    w = gg.complete(2048, 1, 20, 3)               # narrow weights: ties everywhere
+    d = orc.fw_i32(w)
+    got = gpu_successors(dev, w, d)
+    assert np.array_equal(got, orc.successors(w, d, INF))

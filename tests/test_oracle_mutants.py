@@ -59,6 +59,11 @@ MUTANTS = {
     "bf_cycle_never": ("    if (!changed) return 0;\n  }\n  return 1;",
                        "    if (!changed) return 0;\n  }\n  return 0;"),
     "bf_edge_target_is_source": ("const int64_t v = col[e];", "const int64_t v = u;"),
+    # successors
+    "succ_largest_tie": ("if (arg < 0 || cand < best) { best = cand; arg = u; }",
+                         "if (arg < 0 || cand <= best) { best = cand; arg = u; }"),
+    "succ_self_allowed": ("if (u == i || w[i * ld + u] == inf || d[u * ld + j] == inf) continue;",
+                          "if (w[i * ld + u] == inf || d[u * ld + j] == inf) continue;"),
     # min-plus product
     "mp_transposed_b": ("const int64_t btj = b[t * ldb + j];", "const int64_t btj = b[j * ldb + t];"),
     "mp_ignores_c": ("        if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;\n      }\n    }\n}\n\nvoid oracle_minplus_f64",
@@ -171,6 +176,14 @@ def _battery_minplus(o: oracle.Oracle) -> None:
         assert np.array_equal(d, o.fw_i32(w).astype(np.int64))
 
 
+def _battery_successors(o: oracle.Oracle) -> None:
+    g = read_golden("hand4_fw.txt", INF)
+    assert np.array_equal(o.successors(g["input"], g["final"], INF), g["successors"])
+    w = gg.grid(4, 5)
+    nxt = o.successors(w, o.fw_i32(w), INF)
+    assert nxt[19, 0] == 14 and nxt[0, 19] == 1 and nxt[7, 7] == 7
+
+
 def _build_variant(tmp_path, name, edit):
     src = open(oracle.SRC).read()
     if edit is not None:
@@ -190,6 +203,7 @@ def test_battery_passes_on_unmodified_oracle(tmp_path):
     _battery_guarded(o)
     _battery_bellman_ford(o)
     _battery_minplus(o)
+    _battery_successors(o)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -200,3 +214,4 @@ def test_battery_catches_mutant(tmp_path, name):
         _battery_guarded(o)
         _battery_bellman_ford(o)
         _battery_minplus(o)
+        _battery_successors(o)

@@ -486,3 +486,76 @@ def test_minplus_float_with_ieee_inf(orc):
     got = orc.minplus(c, a, b)
     want = np.min(a[:, :, None] + b[None, :, :], axis=1)   # every candidate at once
     assert np.array_equal(got, want)
+
+
+# ---- successors (path reconstruction) ---------------------------------------
+
+def test_successors_hand_example(orc):
+    g = read_golden("hand4_fw.txt", INF)
+    got = orc.successors(g["input"], g["final"], INF)
+    assert np.array_equal(got, g["successors"])
+
+
+def all_shortest_first_hops(w, inf):
+    """Brute force: the set of first vertices over every shortest simple
+    path i -> j (n <= 7)."""
+    n = w.shape[0]
+    best = brute_force_apsp(w, inf)
+    hops = [[set() for _ in range(n)] for _ in range(n)]
+    for s in range(n):
+        stack = [(s, 0, 1 << s, -1)]
+        while stack:
+            u, dist, seen, first = stack.pop()
+            for v in range(n):
+                if v == u or w[u, v] == inf or seen >> v & 1:
+                    continue
+                nd = dist + int(w[u, v])
+                f = v if first < 0 else first
+                if nd == best[s][v]:
+                    hops[s][v].add(f)
+                stack.append((v, nd, seen | (1 << v), f))
+    return best, hops
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_successors_are_the_smallest_shortest_first_hop(orc, seed):
+    # positive weights with many ties (weights in 1..3)
+    rng = np.random.default_rng(60000 + seed)
+    n = int(rng.integers(2, 8))
+    w = random_small_graph(rng, n, [0.3, 0.6][seed % 2], 3, INF)
+    w = np.where((w == 0) & ~np.eye(n, dtype=bool), 1, w)   # strictly positive weights
+    best, hops = all_shortest_first_hops(w, INF)
+    d = orc.fw_i32(w)
+    nxt = orc.successors(w, d, INF)
+    for i in range(n):
+        for j in range(n):
+            if i == j:
+                assert nxt[i, j] == i
+            elif best[i][j] == INF:
+                assert nxt[i, j] == -1
+            else:
+                assert nxt[i, j] == min(hops[i][j])
+
+
+def test_successors_on_a_grid_closed_form(orc):
+    # unit grid, vertex r*C + c: the smallest neighbour index that moves closer
+    # is up (r - 1) if the target row is above, else left, else right, else down
+    R, C = 6, 7
+    w = gg.grid(R, C)
+    d = orc.fw_i32(w)
+    nxt = orc.successors(w, d, INF)
+    for a in range(R * C):
+        ra, ca = divmod(a, C)
+        for b in range(R * C):
+            rb, cb = divmod(b, C)
+            if a == b:
+                want = a
+            elif rb < ra:
+                want = a - C
+            elif cb < ca:
+                want = a - 1
+            elif cb > ca:
+                want = a + 1
+            else:
+                want = a + C
+            assert nxt[a, b] == want, (a, b)
