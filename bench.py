@@ -118,6 +118,9 @@ def cpu_baseline(w, target_s: float):
     per_pivot = run(probe) / probe
     k = int(max(1, min(n, target_s / max(per_pivot, 1e-9))))
     dt = run(k)
+    if dt < 0.6 * target_s and k < n:  # the short probe over-estimated the per-pivot time
+        k = int(max(1, min(n, k * target_s / max(dt, 1e-9))))
+        dt = run(k)
     return {
         "value": k * n * n / dt,
         "unit": "relaxations/s",
