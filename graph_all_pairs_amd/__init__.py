@@ -60,8 +60,8 @@ EXPORTS = (
     "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
     "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
     "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
-    "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_successors_i32", "apsp_successors_f32",
-    "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
+    "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_fw_host_plan", "apsp_successors_i32",
+    "apsp_successors_f32", "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
 )
 
 _lib = None
@@ -121,6 +121,7 @@ def load(path: str | None = None):
         "apsp_minplus_gemm_f32": ([vp, i64, vp, i64, vp, i64, i64, i64, i64, f32, vp], ctypes.c_int),
         "apsp_fw_host_i32": ([vp, i64, i64, i32, i64, vp, lp], ctypes.c_int),
         "apsp_fw_host_f32": ([vp, i64, i64, f32, i64, vp, lp], ctypes.c_int),
+        "apsp_fw_host_plan": ([i64, i64, i64, lp, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
         "apsp_successors_i32": ([vp, i64, vp, i64, vp, i64, i64, i32, vp], ctypes.c_int),
         "apsp_successors_f32": ([vp, i64, vp, i64, vp, i64, i64, f32, vp], ctypes.c_int),
         "apsp_fw_paths_i32": ([vp, i64, vp, i64, i64, i32, vp], ctypes.c_int),
@@ -199,6 +200,15 @@ def apsp_fw_host_f32(h_ptr, n, ld, inf, device_bytes=0, stream=0):
     st = load().apsp_fw_host_f32(h_ptr or None, n, ld, inf, device_bytes, stream or None,
                                  ctypes.byref(blk))
     return int(st), int(blk.value)
+
+
+def apsp_fw_host_plan(n, elem_bytes, device_bytes):
+    """(status, outer block S, panel sets: 0 in-core, 1 or 2)."""
+    blk = ctypes.c_int64(0)
+    sets = ctypes.c_int32(0)
+    st = load().apsp_fw_host_plan(n, elem_bytes, device_bytes, ctypes.byref(blk),
+                                  ctypes.byref(sets))
+    return int(st), int(blk.value), int(sets.value)
 
 
 def apsp_successors_i32(w, ldw, d, ldd, nxt, ldn, n, inf, stream=0) -> int:

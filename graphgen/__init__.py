@@ -424,8 +424,9 @@ WORKLOADS = {
 # Host-resident matrices for the out-of-core path: the matrix stays in
 # (pinned) host memory and streams through a device budget smaller than it.
 HOST_WORKLOADS = {
+    # a 4 GiB matrix in pinned host memory, 3 GiB of device memory to run in
     "host-complete-32768-i32": dict(kind="complete", n=32768, wlo=1, whi=10000, seed=6,
-                                    outer_block=8192),
+                                    device_budget=3 << 30),
 }
 
 

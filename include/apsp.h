@@ -176,19 +176,25 @@ int apsp_minplus_gemm_f32(float *C, int64_t ldc, const float *A, int64_t lda, co
  * All-pairs shortest paths of a matrix in HOST memory, for graphs larger
  * than device memory ("Katz and Kider" page, section 4.6.1: the in-core
  * method needs the whole graph in global memory).  The blocked rounds run on
- * outer blocks of S pivots (S a multiple of 128, the largest that fits the
- * device budget): the S x S diagonal block is closed on the device by the
- * in-core rounds, the S-wide pivot-row and pivot-column panels are updated
- * and held in device memory, and every other S x S super-tile streams to the
- * device, takes its min-plus product of depth S, and streams back.
+ * outer blocks of S pivots (S a multiple of 128): the S x S diagonal block is
+ * closed on the device by the in-core rounds, the S-wide pivot-row and
+ * pivot-column panels are updated and held in device memory, and every other
+ * S x S super-tile streams to the device, takes its min-plus product of
+ * depth S, and streams back.  The panels go back to the host while the
+ * super-tiles are computed.
  *   h, n, ld, inf   the matrix, in place in host memory, with the contract
  *                   of apsp_fw_i32 / apsp_fw_f32 (element (i,j) at h[i*ld+j]).
  *                   Allocate it pinned (hipHostMalloc) for copies that
  *                   overlap the products; pageable memory works, slower.
  *   device_bytes    device memory the call may use (0: half of the free
- *                   memory); about 4 (2 S n + 4 S^2) bytes are taken.  A
- *                   budget too small for S = 128 returns APSP_ERR_RANGE.
- *   outer_block     optional output (may be NULL): the S used.
+ *                   memory).  How it is used is apsp_fw_host_plan's answer:
+ *                   a matrix that fits is copied in whole and computed
+ *                   in-core; else S and one or two panel sets are chosen to
+ *                   fit (about 4 (2 S n + 4 S^2) bytes with one set,
+ *                   4 (4 S n + 4 S^2) with two).  A budget too small for
+ *                   S = 128 returns APSP_ERR_RANGE with the matrix untouched.
+ *   outer_block     optional output (may be NULL): the S used (n rounded up
+ *                   to 128 when in-core).
  * int32 matrices compute in binary32 when that is exact, as for apsp_fw_i32
  * (the arithmetic policy applies), decided by a device scan streamed over
  * the matrix first.  Results equal apsp_fw_i32 / apsp_fw_f32 on the same
@@ -200,6 +206,24 @@ int apsp_fw_host_i32(int32_t *h, int64_t n, int64_t ld, int32_t inf, int64_t dev
                      void *stream, int64_t *outer_block);
 int apsp_fw_host_f32(float *h, int64_t n, int64_t ld, float inf, int64_t device_bytes,
                      void *stream, int64_t *outer_block);
+
+/*
+ * How apsp_fw_host_* would run an n x n matrix of elem_bytes-byte elements
+ * (4: int32 or float) in device_bytes of device memory, without running it:
+ *   *panel_sets = 0   the matrix fits: in-core (outer_block = n rounded up
+ *                     to 128);
+ *               = 1   outer block S, one panel set, reloaded every round;
+ *               = 2   outer block S, two panel sets: the next round's panels
+ *                     are computed in place, never reloaded.
+ * S is the largest multiple of 128 that fits, then lowered to the smallest
+ * multiple of 128 with the same number of rounds.  Two sets are taken when
+ * they fit at S >= min(S with one set, 4096).  Host logic only: with
+ * device_bytes > 0 it makes no HIP call; 0 asks the device for half of its
+ * free memory.  Returns APSP_ERR_RANGE when S = 128 does not fit,
+ * APSP_ERR_INVALID_VALUE for bad arguments; outputs may be NULL.
+ */
+int apsp_fw_host_plan(int64_t n, int64_t elem_bytes, int64_t device_bytes, int64_t *outer_block,
+                      int32_t *panel_sets);
 
 /*
  * Path reconstruction: the successor (first-hop) matrix.  For i != j,

@@ -235,6 +235,62 @@ def test_host_argument_errors(lib, args):
     assert ga.apsp_fw_host_i32(0, 0, 1, 100)[0] == ga.APSP_OK
 
 
+def _plan_by_search(n, budget):
+    """What the host-resident call should choose, by plain search over the
+    multiples of 128: in-core when the matrix fits; else the largest S whose
+    buffers fit with one or two panel sets (two when S2 >= min(S1, 4096)),
+    lowered to the smallest S with the same number of outer rounds."""
+    ldr = (n + 3) // 4 * 4
+    n128 = (n + 127) // 128 * 128
+    if 4 * n * ldr <= budget:
+        return ga.APSP_OK, n128, 0
+
+    def need(S, sets):
+        return 4 * (sets * (S * ldr + n * S) + 4 * S * S)
+
+    def largest(sets):
+        best = 0
+        for S in range(128, n128 + 1, 128):
+            if need(S, sets) <= budget:
+                best = S
+        return best
+    s1, s2 = largest(1), largest(2)
+    if s1 == 0:
+        return ga.APSP_ERR_RANGE, 0, 0
+    sets, top = (2, s2) if s2 and s2 >= min(s1, 4096) else (1, s1)
+    rounds = -(-n // top)
+    S = 128
+    while -(-n // S) > rounds:
+        S += 128
+    assert need(S, sets) <= budget
+    return ga.APSP_OK, S, sets
+
+
+@pytest.mark.parametrize("n", [1, 5, 127, 128, 129, 1000, 4099, 32768, 100_003])
+@pytest.mark.parametrize("frac", [0.0, 0.01, 0.05, 0.2, 0.5, 0.75, 0.99, 1.0, 2.0])
+def test_host_plan_matches_a_plain_search(lib, n, frac):
+    ldr = (n + 3) // 4 * 4
+    budget = max(1, int(frac * 4 * n * ldr))
+    want = _plan_by_search(n, budget)
+    assert ga.apsp_fw_host_plan(n, 4, budget) == want
+
+
+def test_host_plan_named_cases(lib):
+    n = 32768
+    # 3 GiB for a 4 GiB matrix: two sets, 7 balanced rounds
+    st, S, sets = ga.apsp_fw_host_plan(n, 4, 3 << 30)
+    assert (st, sets) == (ga.APSP_OK, 2) and S % 128 == 0 and -(-n // S) == 7
+    # exactly the matrix: in-core
+    assert ga.apsp_fw_host_plan(n, 4, 4 * n * n) == (ga.APSP_OK, n, 0)
+    # a tight budget keeps one set at a larger S
+    st, S, sets = ga.apsp_fw_host_plan(n, 4, 4 * (2 * 1024 * n + 4 * 1024 * 1024))
+    assert (st, S, sets) == (ga.APSP_OK, 1024, 1)
+    assert ga.apsp_fw_host_plan(n, 4, 1000)[0] == ga.APSP_ERR_RANGE
+    assert ga.apsp_fw_host_plan(0, 4, 0) == (ga.APSP_OK, 0, 0)
+    for args in ((-1, 4, 100), (5, 8, 100), (5, 4, -1), (2**31 + 1, 4, 100)):
+        assert ga.apsp_fw_host_plan(*args)[0] == ga.APSP_ERR_INVALID_VALUE
+
+
 def test_path_walker_on_host_memory(lib):
     import numpy as np
     # successors of the hand-worked example (tests/golden/hand4_fw.txt)

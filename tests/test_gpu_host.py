@@ -139,51 +139,97 @@ def run_host(w, inf, device_bytes, ld=None):
     return out[:, :n].copy(), blk
 
 
-def budget_for(n, S, itemsize=4):
+def budget_for(n, S, sets=1, itemsize=4):
+    """The device bytes the host-resident call needs at outer block S with
+    one or two panel sets."""
     ldr = (n + 3) // 4 * 4
-    return itemsize * (S * ldr + n * S + 4 * S * S)
+    return itemsize * (sets * (S * ldr + n * S) + 4 * S * S)
 
 
-@pytest.mark.parametrize("n,S", [(1, 128), (100, 128), (300, 128), (1000, 256), (1000, 384),
-                                 (1031, 512), (2000, 2048)])
+# (n, budget, the plan the library must pick: outer block, panel sets).
+# Sets 0: the matrix fits and runs in-core; 1: one panel set reloaded every
+# outer round; 2: the next round's panels computed in place.
+HOST_CASES = [
+    (1, budget_for(1, 128), 128, 0),
+    (100, budget_for(100, 128), 128, 0),
+    (300, budget_for(300, 128), 384, 0),
+    (1000, budget_for(1000, 256), 256, 1),             # 4 rounds, ragged
+    (2000, budget_for(2000, 256), 256, 1),             # 8 rounds, ragged
+    (2000, budget_for(2000, 384, 2), 512, 1),          # 4 rounds, ragged
+    (1000, budget_for(1000, 128, 2), 128, 2),          # 8 rounds, ragged
+    (1031, budget_for(1031, 128, 2), 128, 2),          # 9 rounds, 7-wide tail
+]
+
+
+@pytest.mark.parametrize("n,budget,S,sets", HOST_CASES)
 @pytest.mark.parametrize("policy", [ga.APSP_ARITH_AUTO, ga.APSP_ARITH_INT32,
                                     ga.APSP_ARITH_F32_WHEN_EXACT])
-def test_host_int32_matches_oracle(dev, n, S, policy):
-    print(f"case host i32 n={n} S={S} policy={policy}", flush=True)
+def test_host_int32_matches_oracle(dev, n, budget, S, sets, policy):
+    print(f"case host i32 n={n} budget={budget} policy={policy}", flush=True)
+    assert ga.apsp_fw_host_plan(n, 4, budget) == (ga.APSP_OK, S, sets)
     w = gg.erdos_renyi(n, 0.02 if n > 100 else 0.2, 1, 100, 100 + n)
     with ga.int32_arith(policy):
-        got, blk = run_host(w, INF, budget_for(n, S))
-    assert blk == min(S, (n + 127) // 128 * 128)
+        got, blk = run_host(w, INF, budget)
+    assert blk == S
     assert np.array_equal(got, oracle.fw_i32(w))
 
 
-def test_host_int32_large_weights_and_padding(dev):
+@pytest.mark.parametrize("sets", [1, 2])
+def test_host_int32_large_weights_and_padding(dev, sets):
     # weights above 2^24: int32 arithmetic throughout; ld > n with a canary
-    print("case host i32 large weights, ld > n", flush=True)
+    print(f"case host i32 large weights, ld > n, sets={sets}", flush=True)
     n = 900
+    budget = budget_for(n, 256 if sets == 1 else 128, sets)
+    S = ga.apsp_fw_host_plan(n, 4, budget)[1]
+    assert ga.apsp_fw_host_plan(n, 4, budget) == (ga.APSP_OK, S, sets)
     w = gg.erdos_renyi(n, 0.01, 1, 50_000_000, 7)
-    got, blk = run_host(w, INF, budget_for(n, 256), ld=n + 13)
-    assert blk == 256 and np.array_equal(got, oracle.fw_i32(w))
+    got, blk = run_host(w, INF, budget, ld=n + 13)
+    assert blk == S and np.array_equal(got, oracle.fw_i32(w))
 
 
-def test_host_complete_graph_equals_in_core(dev):
-    print("case host complete n=3000 against apsp_fw_i32", flush=True)
-    n = 3000
+@pytest.fixture(scope="module")
+def complete_20481():
+    # n = 5 * 4096 + 1, a 1.6 GiB matrix (about 16 s to generate), with its
+    # in-core distances from apsp_fw_i32 in HBM
+    print("generating complete n=20481 and its in-core distances", flush=True)
+    n = 20481
     w = gg.complete(n, 1, 10000, 5)
-    got, blk = run_host(w, INF, budget_for(n, 1024))
-    assert blk == 1024
-    t = torch.from_numpy(w).to(dev)
+    t = torch.from_numpy(w).to("cuda:0")
     ga.fw(t, INF)
-    assert np.array_equal(got, t.cpu().numpy())
-    rows = np.array([0, 1, 1499, 2999])
+    d = t.cpu().numpy()
+    del t
+    return w, d
+
+
+@pytest.mark.parametrize("policy", [ga.APSP_ARITH_AUTO, ga.APSP_ARITH_INT32])
+def test_host_two_sets_at_scale_equals_in_core(dev, complete_20481, policy):
+    # just over the budget: two panel sets at S = 4096, balanced to 6 rounds
+    # of 3456 (the last 3201 wide); against the in-core result and the
+    # oracle's single-source rows
+    print(f"case host complete n=20481 two sets policy={policy}", flush=True)
+    w, want = complete_20481
+    n = w.shape[0]
+    budget = budget_for(n, 4096, 2)
+    assert ga.apsp_fw_host_plan(n, 4, budget) == (ga.APSP_OK, 3456, 2)
+    with ga.int32_arith(policy):
+        got, blk = run_host(w, INF, budget)
+    assert blk == 3456
+    assert np.array_equal(got, want)
+    rows = np.array([0, 1, 3455, 3456, 17280, 20480])
     assert np.array_equal(got[rows], oracle.sssp_rows_i32(w, INF, rows))
 
 
-@pytest.mark.parametrize("n,S", [(257, 128), (1000, 256)])
-def test_host_float32_matches_oracle(dev, n, S):
-    print(f"case host f32 n={n} S={S}", flush=True)
+@pytest.mark.parametrize("n,budget,S,sets", [
+    (500, budget_for(500, 128), 128, 1),
+    (1000, budget_for(1000, 256), 256, 1),
+    (1000, budget_for(1000, 128, 2), 128, 2),
+    (600, 4 * 600 * 600, 640, 0),
+])
+def test_host_float32_matches_oracle(dev, n, budget, S, sets):
+    print(f"case host f32 n={n} S={S} sets={sets}", flush=True)
+    assert ga.apsp_fw_host_plan(n, 4, budget) == (ga.APSP_OK, S, sets)
     w = gg.complete_f32(n, 40 + n)
-    got, blk = run_host(w, float("inf"), budget_for(n, S))
+    got, blk = run_host(w, float("inf"), budget)
     want = oracle.fw_f64(w.astype(np.float64))
     rel = np.abs(got.astype(np.float64) - want) / np.maximum(np.abs(want), 1e-30)
     assert blk == S and float(rel.max()) <= 1e-5
@@ -201,8 +247,8 @@ def test_host_budget_too_small_is_a_range_error(dev):
 
 def test_host_pageable_memory_works(dev):
     print("case host pageable", flush=True)
-    n = 600
+    n = 1000
     w = gg.erdos_renyi(n, 0.02, 1, 100, 9)
     h = torch.from_numpy(w.copy())           # not pinned
-    ga.fw_host(h, INF, budget_for(n, 256))
+    assert ga.fw_host(h, INF, budget_for(n, 128, 2)) == 128
     assert np.array_equal(h.numpy(), oracle.fw_i32(w))
