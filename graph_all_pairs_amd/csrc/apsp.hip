@@ -574,11 +574,9 @@ __global__ void __launch_bounds__(kThreads) convert_i32(int32_t* __restrict__ d,
                                                         int64_t ld, int32_t inf,
                                                         const int32_t* __restrict__ s) {
   if (!f32_exact(s, n)) return;
-  const float finf = (float)inf;
   auto conv = [&](int32_t v) -> int32_t {
-    if (TO_F32) return __float_as_int(v == inf ? __builtin_inff() : (float)v);
-    const float f = __int_as_float(v);
-    return f >= finf ? inf : (int32_t)f;
+    if (TO_F32) return __float_as_int(i32_to_f32(v, inf));
+    return f32_to_i32(__int_as_float(v), inf);
   };
   const int64_t quads = (n + 3) / 4;
   for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
@@ -744,13 +742,9 @@ __global__ void __launch_bounds__(kThreads) scan_signed_i32(const int32_t* __res
 template <bool VEC, bool TO_F32>
 __global__ void __launch_bounds__(kThreads) signed_convert(int32_t* __restrict__ d, int64_t n,
                                                            int64_t ld, int32_t inf) {
-  const float finf = (float)inf;
   auto conv = [&](int32_t v) -> int32_t {
-    if (TO_F32) return __float_as_int(v == inf ? __builtin_inff() : (float)v);
-    const float f = __int_as_float(v);
-    if (f >= finf) return inf;
-    if (!(f > -2147483648.0f)) return INT32_MIN;  // also catches NaN
-    return (int32_t)f;
+    if (TO_F32) return __float_as_int(i32_to_f32(v, inf));
+    return f32_to_i32(__int_as_float(v), inf);
   };
   const int64_t quads = (n + 3) / 4;
   for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {

@@ -89,20 +89,15 @@ __global__ void __launch_bounds__(256) hs_scan(const int32_t* __restrict__ t, in
 }
 
 // In place over a rows x cols tile: int32 <-> binary32 (inf <-> +infinity;
-// back from binary32 anything >= inf is inf).
+// back from binary32 anything >= inf is inf, compared as integers).
 template <bool TO_F32>
 __global__ void __launch_bounds__(256) hs_convert(int32_t* __restrict__ t, int64_t ld, int64_t rows,
                                                   int64_t cols, int32_t inf) {
-  const float finf = (float)inf;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
     for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) {
       int32_t* p = t + r * ld + c;
-      if (TO_F32) {
-        *p = __float_as_int(*p == inf ? __builtin_inff() : (float)*p);
-      } else {
-        const float f = __int_as_float(*p);
-        *p = f >= finf ? inf : (int32_t)f;
-      }
+      if (TO_F32) *p = __float_as_int(i32_to_f32(*p, inf));
+      else *p = f32_to_i32(__int_as_float(*p), inf);
     }
 }
 
@@ -136,12 +131,9 @@ unsigned conv_grid(int64_t rows) { return (unsigned)std::min<int64_t>(std::max<i
 __global__ void __launch_bounds__(256) hs_to_i32(int32_t* __restrict__ dst, int64_t ldd,
                                                  const float* __restrict__ src, int64_t lds,
                                                  int64_t rows, int64_t cols, int32_t inf) {
-  const float finf = (float)inf;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
-    for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) {
-      const float f = src[r * lds + c];
-      dst[r * ldd + c] = f >= finf ? inf : (int32_t)f;
-    }
+    for (int64_t c = threadIdx.x; c < cols; c += blockDim.x)
+      dst[r * ldd + c] = f32_to_i32(src[r * lds + c], inf);
 }
 
 // How the call runs, from n, the element size and the device budget.

@@ -36,6 +36,23 @@ __device__ __forceinline__ float mp_min3(float a, float b, float c) {
   return r;
 }
 
+// An int32 matrix computed in binary32 (only when that is exact): entry in,
+// and result back.  "No edge" (the sentinel inf) becomes +infinity.  Back,
+// the value is compared with inf as an integer, not as (float)inf: 2^24 + 1
+// rounds to 2^24 in binary32, so a float comparison would turn an exact
+// distance of 2^24 into inf.  +infinity, and anything not below 2^31, is
+// inf; values not above -2^31 (only after a negative cycle) saturate, and
+// NaN goes there too.
+__device__ __forceinline__ float i32_to_f32(int32_t v, int32_t inf) {
+  return v == inf ? __builtin_inff() : (float)v;
+}
+__device__ __forceinline__ int32_t f32_to_i32(float f, int32_t inf) {
+  if (!(f > -2147483648.0f)) return INT32_MIN;
+  if (!(f < 2147483648.0f)) return inf;
+  const int32_t v = (int32_t)f;
+  return v >= inf ? inf : v;
+}
+
 template <typename T> struct Vec4;
 template <> struct Vec4<int32_t> { using type = int4; };
 template <> struct Vec4<float> { using type = float4; };
