@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <functional>
 #include <type_traits>
 
 #include "apsp.h"
@@ -50,6 +51,7 @@ using namespace apsp_dev;
 
 constexpr int64_t kB = 128;
 constexpr int kSlots = 3;
+constexpr int kRetryInt32 = -1000;  // private: binary32 turned out not to be exact
 constexpr int64_t kExactLimit = int64_t(1) << 24;
 
 struct HostScan {
@@ -193,7 +195,11 @@ int plan_for(int64_t n, int64_t esz, int64_t budget, Plan* p) {
 }
 
 // The rounds with compute type CT on matrix element type E (int32 -> int32,
-// int32 -> binary32, float -> float), with `sets` panel sets.
+// int32 -> binary32, float -> float), with `sets` panel sets.  With two
+// sets, the super-tiles of the next pivot row and column are computed in
+// place in the other set (no copy out and back in), and the parts of the
+// next panels that lie in this round's panels are copied across on the
+// device.
 //
 // Streams: `s` runs the panel work (load, closure, Phase 2); three slot
 // streams run the Phase-3 super-tiles.  Each round ends with `s` waiting for
@@ -208,13 +214,17 @@ int plan_for(int64_t n, int64_t esz, int64_t budget, Plan* p) {
 // untouched until the next round's Phase 3, so they go back during the next
 // round's closure and Phase 2 (on the first slot stream, staged through its
 // tile buffer), when nothing else leaves the device; the last round's go
-// back at the end.  With two sets, the super-tiles of the next pivot row and column are
-// computed in place in the other set (no copy out and back in), and the parts
-// of the next panels that lie in this round's panels are copied across on
-// the device.
+// back at the end.
+//
+// `gate`, when given, is asked once, after round 0's Phase 2 has been issued
+// and before anything is written to the host or any Phase-3 work is issued:
+// APSP_OK goes on; anything else ends the call with that status
+// (kRetryInt32: the binary32 speculation failed, the host matrix is
+// untouched).
 template <typename E, typename CT>
 int run_rounds(E* h, int64_t n, int64_t ldh, E inf, int64_t S, int sets, bool panels_loaded,
-               char* dev, hipStream_t s, hipStream_t* slot, hipEvent_t* ev) {
+               char* dev, hipStream_t s, hipStream_t* slot, hipEvent_t* ev,
+               const std::function<int()>* gate) {
   constexpr bool kConv = std::is_same_v<E, int32_t> && std::is_same_v<CT, float>;
   const CT cinf = kConv ? CT(__builtin_inff()) : CT(inf);
   const int64_t ldr = (n + 3) & ~int64_t(3);  // row panel leading dimension
@@ -337,6 +347,7 @@ int run_rounds(E* h, int64_t n, int64_t ldh, E inf, int64_t S, int sets, bool pa
       HIP_TRY(copy2d(cp[nx] + K0 * S, S, R + K1, ldr, sk, sk1, hipMemcpyDeviceToDevice, s));
     }
     HIP_TRY(hipEventRecord(ev_panels, s));
+    if (KK == 0 && gate != nullptr && (rc = (*gate)()) != APSP_OK) goto done;
     // -- one set: the panels go back while Phase 3 reads them -----------------
     if (sets == 1) HIP_TRY(write_panels(R, C, K0, sk, tmp, s));
     // -- Phase 3: every other super-tile through the slot streams.  A slot's
@@ -456,8 +467,7 @@ int run_host(E* h, int64_t n, int64_t ldh, E inf, int64_t device_bytes, void* st
   hipEvent_t ev[3 + kSlots] = {};
   char* dev = nullptr;
   HostScan* scan = nullptr;
-  HostScan hs{};
-  bool f32 = false, loaded = false;
+  HostScan* hs = nullptr;  // pinned, so the copy into it stays asynchronous
   for (int i = 0; i < kSlots; ++i)
     if (hipStreamCreateWithFlags(&slot[i], hipStreamNonBlocking) != hipSuccess) {
       rc = hip_failed();
@@ -475,51 +485,78 @@ int run_host(E* h, int64_t n, int64_t ldh, E inf, int64_t device_bytes, void* st
   }
 
   if constexpr (std::is_same_v<E, int32_t>) {
-    // Which arithmetic: stream the matrix through the device once.  The
-    // first round's panels are loaded on the way (row block 0 into the row
-    // panel, column block 0 into the column panel); the other super-tiles
-    // pass through a slot buffer.
+    // Which arithmetic.  Round 0's panels are loaded and scanned first; if
+    // they already rule binary32 out, the call runs in int32 with no further
+    // scan.  Otherwise the rest of the matrix is scanned on the first slot
+    // stream (through its tile buffer) while round 0's closure and Phase 2
+    // run in binary32 on `s`; before round 0 writes anything to the host,
+    // the gate reads the whole scan, and if binary32 is not exact after all
+    // the call starts over in int32 (the panels are reloaded).
     const int policy = apsp_get_int32_arith();
-    if (policy != APSP_ARITH_INT32) {
+    if (policy == APSP_ARITH_INT32) {
+      rc = run_rounds<int32_t, int32_t>(h, n, ldh, inf, S, plan.sets, false, dev, s, slot, ev, nullptr);
+      goto cleanup;
+    }
+    if (hipHostMalloc(reinterpret_cast<void**>(&hs), sizeof(HostScan), hipHostMallocDefault) != hipSuccess) {
+      hs = nullptr;
+      rc = hip_failed();
+      goto cleanup;
+    }
+    {
       E* rp0 = reinterpret_cast<E*>(dev);
       E* cp0 = rp0 + S * ldr;
-      E* buf = cp0 + n * S + S * S;
+      E* buf = cp0 + n * S + S * S;  // the first slot's tile buffer
+      auto exact = [&](const HostScan& x) {
+        return !(x.flags & 2) && (!(x.flags & 1) || (n - 1) * (int64_t)x.maxw <= kExactLimit);
+      };
       hipLaunchKernelGGL(hs_zero, dim3(1), dim3(64), 0, s, scan);
-      for (int64_t r0 = 0; r0 < n && rc == APSP_OK; r0 += S) {
-        const int64_t rows = std::min(S, n - r0);
-        for (int64_t c0 = 0; c0 < n; c0 += S) {
-          const int64_t cols = std::min(S, n - c0);
-          E* dst = buf;
-          int64_t ldd = S;
-          if (r0 == 0) {
-            dst = rp0 + c0;
-            ldd = ldr;
-          } else if (c0 == 0) {
-            dst = cp0 + r0 * S;
-          }
-          if (copy2d(dst, ldd, h + r0 * ldh + c0, ldh, rows, cols, hipMemcpyHostToDevice, s) != hipSuccess) {
-            rc = hip_failed();
-            break;
-          }
-          hipLaunchKernelGGL(hs_scan, dim3(conv_grid(rows)), dim3(256), 0, s, dst, ldd, rows, cols,
-                             r0, c0, inf, scan);
-        }
+      if (copy2d(rp0, ldr, h, ldh, S, n, hipMemcpyHostToDevice, s) != hipSuccess ||
+          copy2d(cp0 + S * S, S, h + S * ldh, ldh, n - S, S, hipMemcpyHostToDevice, s) != hipSuccess) {
+        rc = hip_failed();
+        goto cleanup;
       }
-      if (rc != APSP_OK) goto cleanup;
-      if (hipMemcpyAsync(&hs, scan, sizeof(hs), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipLaunchKernelGGL(hs_scan, dim3(conv_grid(S)), dim3(256), 0, s, rp0, ldr, S, n, int64_t(0),
+                         int64_t(0), inf, scan);
+      hipLaunchKernelGGL(hs_scan, dim3(conv_grid(n - S)), dim3(256), 0, s, cp0 + S * S, S, n - S, S,
+                         S, int64_t(0), inf, scan);
+      if (hipMemcpyAsync(hs, scan, sizeof(HostScan), hipMemcpyDeviceToHost, s) != hipSuccess ||
           hipStreamSynchronize(s) != hipSuccess) {
         rc = hip_failed();
         goto cleanup;
       }
-      f32 = !(hs.flags & 2) && (!(hs.flags & 1) || (n - 1) * (int64_t)hs.maxw <= kExactLimit);
-      // Row block 0 of the column panel was not loaded: the closed diagonal
+      // Row block 0 of the column panel is not loaded: the closed diagonal
       // block is copied there before it is read.
-      loaded = true;
+      if (!exact(*hs)) {
+        rc = run_rounds<int32_t, int32_t>(h, n, ldh, inf, S, plan.sets, true, dev, s, slot, ev, nullptr);
+        goto cleanup;
+      }
+      for (int64_t r0 = S; r0 < n && rc == APSP_OK; r0 += S)
+        for (int64_t c0 = S; c0 < n; c0 += S) {
+          const int64_t rows = std::min(S, n - r0), cols = std::min(S, n - c0);
+          if (copy2d(buf, S, h + r0 * ldh + c0, ldh, rows, cols, hipMemcpyHostToDevice, slot[0]) != hipSuccess) {
+            rc = hip_failed();
+            break;
+          }
+          hipLaunchKernelGGL(hs_scan, dim3(conv_grid(rows)), dim3(256), 0, slot[0], buf, S, rows, cols,
+                             r0, c0, inf, scan);
+        }
+      if (rc != APSP_OK) goto cleanup;
+      if (hipMemcpyAsync(hs, scan, sizeof(HostScan), hipMemcpyDeviceToHost, slot[0]) != hipSuccess) {
+        rc = hip_failed();
+        goto cleanup;
+      }
+      const std::function<int()> gate = [&]() -> int {
+        if (hipStreamSynchronize(slot[0]) != hipSuccess) return hip_failed();
+        return exact(*hs) ? APSP_OK : kRetryInt32;
+      };
+      rc = run_rounds<int32_t, float>(h, n, ldh, inf, S, plan.sets, true, dev, s, slot, ev, &gate);
+      if (rc == kRetryInt32) {
+        (void)hipStreamSynchronize(s);
+        rc = run_rounds<int32_t, int32_t>(h, n, ldh, inf, S, plan.sets, false, dev, s, slot, ev, nullptr);
+      }
     }
-    if (f32) rc = run_rounds<int32_t, float>(h, n, ldh, inf, S, plan.sets, loaded, dev, s, slot, ev);
-    else rc = run_rounds<int32_t, int32_t>(h, n, ldh, inf, S, plan.sets, loaded, dev, s, slot, ev);
   } else {
-    rc = run_rounds<float, float>(h, n, ldh, inf, S, plan.sets, loaded, dev, s, slot, ev);
+    rc = run_rounds<float, float>(h, n, ldh, inf, S, plan.sets, false, dev, s, slot, ev, nullptr);
   }
 
 cleanup:
@@ -529,6 +566,7 @@ cleanup:
   if (dev) (void)hipFreeAsync(dev, s);
   if (scan) (void)hipFreeAsync(scan, s);
   (void)hipStreamSynchronize(s);
+  if (hs) (void)hipHostFree(hs);
   for (auto& e : ev)
     if (e) (void)hipEventDestroy(e);
   for (auto& st : slot)

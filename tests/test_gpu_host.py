@@ -235,6 +235,28 @@ def test_host_float32_matches_oracle(dev, n, budget, S, sets):
     assert blk == S and float(rel.max()) <= 1e-5
 
 
+@pytest.mark.parametrize("sets", [1, 2])
+@pytest.mark.parametrize("late", ["weight-above-2^24", "inf-with-heavy-weight"])
+def test_host_binary32_speculation_falls_back_to_int32(dev, sets, late):
+    # Round 0's panels (row and column block 0) are exact in binary32, the
+    # rest of the matrix is not: the call starts round 0 in binary32 while it
+    # scans the rest, then must start over in int32 with the host untouched.
+    print(f"case host speculation fallback sets={sets} late={late}", flush=True)
+    n = 1000
+    budget = budget_for(n, 256) if sets == 1 else budget_for(n, 128, 2)
+    S = ga.apsp_fw_host_plan(n, 4, budget)[1]
+    assert ga.apsp_fw_host_plan(n, 4, budget) == (ga.APSP_OK, S, sets)
+    w = gg.erdos_renyi(n, 1.0, 1, 100, 41)
+    if late == "weight-above-2^24":
+        w[900, 950] = 50_000_000
+    else:
+        w[850, 860] = INF            # an inf entry, and (n - 1) * 20000 > 2^24
+        w[870, 880] = 20000
+    assert (w[:S] < 100_000).all() and (w[:, :S] < 100_000).all()
+    got, blk = run_host(w, INF, budget)
+    assert blk == S and np.array_equal(got, oracle.fw_i32(w))
+
+
 def test_host_budget_too_small_is_a_range_error(dev):
     print("case host budget too small", flush=True)
     w = gg.erdos_renyi(500, 0.05, 1, 10, 3)
