@@ -515,7 +515,7 @@ def bench_host(args) -> int:
         "traffic": None,
         "pcie_bytes_per_step": moved,
         "pcie_gb_per_s": moved / (wall / args.steps) / 1e9,
-        "note": "whole-job rate: the product kernel alone is measured in DESIGN.md",
+        "note": "whole-job rate (products, closures and PCIe transfers together)",
     }
     cpu = None
     if not args.no_cpu_baseline:
@@ -626,8 +626,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is designed but not implemented)", file=sys.stderr)
         return 2
 
     import numpy as np
