@@ -10,10 +10,14 @@
 // Algorithm 16): the graph's matrix is loaded into registers, closed two
 // pivots per barrier, and stored.
 //
-// Size classes (padded edge NB, micro-tile RT x RT, threads (NB/RT)^2):
-//   n <= 32:  NB = 32,  RT = 4,  64 threads (one wave per graph)
-//   n <= 64:  NB = 64,  RT = 8,  64 threads
-//   n <= 128: NB = 128, RT = 8,  256 threads
+// Size classes: the padded edge NB is n rounded up to a multiple of 8 (at
+// least 16), with an RT x RT micro-tile per thread and (NB/RT)^2 threads:
+//   NB = 16, 24, 32:      RT = 4, 16 / 36 / 64 threads (one wave per graph);
+//   NB = 40, 48, ..., 128: RT = 8, 25 ... 256 threads (1 to 4 waves).
+// A graph costs NB/2 pivot-pair steps of the same per-thread work, and the
+// waves it occupies set how many graphs share a CU, so every multiple of 8
+// is its own class (n = 100 runs as NB = 104: 3 waves and 52 steps, against
+// 4 waves and 64 steps at NB = 128).
 // Rows and columns n .. NB-1 are isolated vertices: they load as inf and are
 // never stored, so the closure of the padded block restricted to [0, n) is
 // the closure of the graph.
@@ -128,9 +132,24 @@ int run_batched(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T in
   if (st != APSP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool vec = (reinterpret_cast<uintptr_t>(d) % 16 == 0) && ld % 4 == 0 && stride % 4 == 0;
-  if (n <= 32) launch<T, 32, 4>(d, batch, n, ld, stride, inf, vec, s);
-  else if (n <= 64) launch<T, 64, 8>(d, batch, n, ld, stride, inf, vec, s);
-  else launch<T, 128, 8>(d, batch, n, ld, stride, inf, vec, s);
+  switch ((n + 7) / 8) {
+    case 1:
+    case 2: launch<T, 16, 4>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 3: launch<T, 24, 4>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 4: launch<T, 32, 4>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 5: launch<T, 40, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 6: launch<T, 48, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 7: launch<T, 56, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 8: launch<T, 64, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 9: launch<T, 72, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 10: launch<T, 80, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 11: launch<T, 88, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 12: launch<T, 96, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 13: launch<T, 104, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 14: launch<T, 112, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 15: launch<T, 120, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    default: launch<T, 128, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+  }
   return apsp_detail_launch_status();
 }
 

@@ -19,7 +19,10 @@ pytestmark = pytest.mark.gpu
 
 INF = gg.INF_I32
 F32_RTOL = 1e-5
-SIZES = [1, 2, 3, 5, 16, 31, 32, 33, 47, 63, 64, 65, 100, 127, 128]
+# every size class (n rounded up to a multiple of 8, at least 16) at its edge
+# and one past it, plus a few sizes inside classes
+SIZES = [1, 2, 3, 5, 8, 9, 16, 17, 24, 25, 31, 32, 33, 40, 41, 47, 48, 49, 56, 57, 63, 64, 65,
+         72, 73, 80, 81, 88, 89, 96, 97, 100, 104, 105, 112, 113, 120, 121, 127, 128]
 
 
 @pytest.fixture(scope="module")
@@ -79,7 +82,7 @@ def test_batched_i32_er_exact(dev, n):
     assert np.array_equal(got, oracle.default().fw_batched_i32(w))
 
 
-@pytest.mark.parametrize("n", [4, 32, 64, 96, 128])
+@pytest.mark.parametrize("n", [4, 32, 48, 64, 80, 96, 112, 128])
 def test_batched_i32_complete_padded_layout(dev, n):
     # ld > n and a gap between graphs; the smallest legal stride too
     print(f"batched i32 complete n={n}", flush=True)
@@ -89,7 +92,7 @@ def test_batched_i32_complete_padded_layout(dev, n):
     assert np.array_equal(run_batched(dev, w, INF, ld=n + 3), want)   # stride = (n-1)*ld + n
 
 
-@pytest.mark.parametrize("n", [8, 64, 128])
+@pytest.mark.parametrize("n", [8, 48, 64, 90, 128])
 def test_batched_i32_unaligned_scalar_path(dev, n):
     print(f"batched i32 unaligned n={n}", flush=True)
     w = gg.erdos_renyi_batch(11, n, 0.3, 1, 50, 300 + n)
@@ -109,7 +112,7 @@ def test_batched_i32_rings_closed_form(dev):
         assert all(np.array_equal(got[g], want) for g in range(9))
 
 
-@pytest.mark.parametrize("n", [5, 32, 64, 100, 128])
+@pytest.mark.parametrize("n", [5, 32, 40, 64, 72, 100, 128])
 def test_batched_f32_matches_oracle_and_single_entry(dev, n):
     print(f"batched f32 n={n}", flush=True)
     w = gg.complete_f32_batch(13, n, 400 + n)
