@@ -20,9 +20,23 @@
 // (double buffered), u runs in increasing order and a candidate replaces the
 // pair only when strictly smaller, so the smallest u wins ties.  W[i][i] is
 // staged as inf (u != i).  Per candidate: add, compare, two selects.
+//
+// Sparse weights.  Only u with w(i, u) < inf can win (any other candidate is
+// >= inf and never replaces the running value, which starts at inf), so for
+// a matrix with at most n^2 / 16 finite off-diagonal weights a second kernel
+// tries only the neighbours of i: one workgroup per row gathers the row's
+// neighbours into LDS in increasing u (2048 at a time), then streams row u
+// of D for each of them, 4 columns per thread, with the same strict
+// comparison.  The result is the same matrix.  A row with more neighbours
+// takes several gathers; between them the running value of a column is
+// recomputed from the stored index with the same single add.  A count kernel
+// adds up the finite weights into 8 bytes of stream-ordered scratch, and both
+// kernels read it and return at once unless they are the one for this
+// matrix, so the choice costs no host synchronisation.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "apsp.h"
@@ -62,7 +76,9 @@ __device__ __forceinline__ void ld4(const T* __restrict__ p, int64_t ld, int64_t
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_t ldd,
-           int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf, uint32_t tiles_per_row) {
+           int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf, uint32_t tiles_per_row,
+           const unsigned long long* __restrict__ edges, unsigned long long max_sparse) {
+  if (*edges <= max_sparse) return;  // the sparse kernel takes this matrix
   __shared__ __attribute__((aligned(16))) T lds[4 * kKC * kLd];
   T* sA = lds;                  // [2][kKC][kLd]: sA[t][row] = W[row0 + row][u0 + t]
   T* sB = lds + 2 * kKC * kLd;  // [2][kKC][kLd]: sB[t][col] = D[u0 + t][col0 + col]
@@ -167,6 +183,125 @@ successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_
     }
 }
 
+__global__ void __launch_bounds__(64) succ_zero(unsigned long long* __restrict__ edges) {
+  if (threadIdx.x == 0) *edges = 0;
+}
+
+// The number of finite off-diagonal weights, w[i][u] < inf with u != i.
+template <typename T>
+__global__ void __launch_bounds__(256) succ_count(const T* __restrict__ W, int64_t ldw, int64_t n,
+                                                  T inf, unsigned long long* __restrict__ edges) {
+  unsigned long long c = 0;
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
+    for (int64_t u = threadIdx.x; u < n; u += blockDim.x) c += (u != i && W[i * ldw + u] < inf);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0 && c) atomicAdd(edges, c);
+}
+
+constexpr int kSThreads = 256;
+constexpr int kSeg = kSThreads * 4;  // row entries gathered, and columns relaxed, per step
+constexpr int kCap = 2 * kSeg;       // neighbours held in LDS at a time
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kSThreads)
+successors_sparse(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_t ldd,
+                  int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf,
+                  const unsigned long long* __restrict__ edges, unsigned long long max_sparse) {
+  if (*edges > max_sparse) return;  // the dense kernel takes this matrix
+  __shared__ int32_t lu[kCap];
+  __shared__ T lw[kCap];
+  __shared__ int32_t wsum[kSThreads / 64];
+  const int64_t i = blockIdx.x;
+  const T* wrow = W + i * ldw;
+  int32_t* nrow = nxt + i * ldn;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t p = 0;  // first row entry not gathered yet
+  bool first = true;
+  for (;;) {
+    // Gather the neighbours in [p, ...) until the next segment would overflow
+    // the list; a segment holds at most kSeg <= kCap of them, so p advances.
+    int32_t cnt = 0;
+    while (p < n) {
+      const int64_t u0 = p + tid * 4;
+      T v[4];
+      ld4<T, VEC>(W, ldw, n, n, i, u0, inf, v);
+      bool f[4];
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = u0 + e < n && u0 + e != i && v[e] < inf;
+        c += f[e];
+      }
+      int x = c;  // inclusive scan over the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[wv] = x;
+      __syncthreads();
+      int base = 0, total = 0;
+#pragma unroll
+      for (int k = 0; k < kSThreads / 64; ++k) {
+        const int sk = wsum[k];
+        base += k < wv ? sk : 0;
+        total += sk;
+      }
+      __syncthreads();  // wsum is rewritten by the next segment
+      if (cnt + total > kCap) break;
+      int pos = cnt + base + x - c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (f[e]) {
+          lu[pos] = (int32_t)(u0 + e);
+          lw[pos] = v[e];
+          ++pos;
+        }
+      cnt += total;
+      p += kSeg;
+    }
+    __syncthreads();  // the list is complete
+    const bool last = p >= n;
+    for (int64_t j0 = 0; j0 < n; j0 += kSeg) {
+      const int64_t j = j0 + tid * 4;
+      if (j >= n) continue;
+      T bv[4];
+      int32_t bu[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bv[e] = inf;
+        bu[e] = -1;
+        if (!first && j + e < n) {
+          bu[e] = nrow[j + e];
+          if (bu[e] >= 0) bv[e] = wrow[bu[e]] + D[(int64_t)bu[e] * ldd + j + e];
+        }
+      }
+#pragma unroll 4
+      for (int32_t t = 0; t < cnt; ++t) {
+        const int32_t u = lu[t];
+        const T wu = lw[t];
+        T dv[4];
+        ld4<T, VEC>(D, ldd, n, n, u, j, inf, dv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const T cand = wu + dv[e];
+          const bool better = cand < bv[e];
+          bv[e] = better ? cand : bv[e];
+          bu[e] = better ? u : bu[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n)
+          nrow[j + e] = !last ? bu[e] : (j + e == i ? (int32_t)i : (bv[e] < inf ? bu[e] : -1));
+    }
+    if (last) break;
+    first = false;
+    __syncthreads();  // the list is rebuilt
+  }
+}
+
 template <typename T>
 bool inf_ok(T inf);
 template <>
@@ -195,14 +330,30 @@ int run_successors(const T* w, int64_t ldw, const T* d, int64_t ldd, int32_t* nx
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = al16(w) && al16(d) && ldw % 4 == 0 && ldd % 4 == 0;
+  unsigned long long* edges = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&edges), sizeof(unsigned long long), s) != hipSuccess) {
+    (void)apsp_detail_launch_status();
+    return APSP_ERR_LAUNCH;
+  }
+  const unsigned long long max_sparse = (unsigned long long)n * (unsigned long long)n / 16;
+  hipLaunchKernelGGL(succ_zero, dim3(1), dim3(64), 0, s, edges);
+  hipLaunchKernelGGL(succ_count<T>, dim3((unsigned)std::min<int64_t>(n, 4096)), dim3(256), 0, s, w,
+                     ldw, n, inf, edges);
   const dim3 grid((unsigned)(tpr * tpr));
-  if (vec)
+  if (vec) {
     hipLaunchKernelGGL((successors<T, true>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt, ldn,
-                       n, inf, (uint32_t)tpr);
-  else
+                       n, inf, (uint32_t)tpr, edges, max_sparse);
+    hipLaunchKernelGGL((successors_sparse<T, true>), dim3((unsigned)n), dim3(kSThreads), 0, s, w, ldw,
+                       d, ldd, nxt, ldn, n, inf, edges, max_sparse);
+  } else {
     hipLaunchKernelGGL((successors<T, false>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt,
-                       ldn, n, inf, (uint32_t)tpr);
-  return apsp_detail_launch_status();
+                       ldn, n, inf, (uint32_t)tpr, edges, max_sparse);
+    hipLaunchKernelGGL((successors_sparse<T, false>), dim3((unsigned)n), dim3(kSThreads), 0, s, w,
+                       ldw, d, ldd, nxt, ldn, n, inf, edges, max_sparse);
+  }
+  const int st_launch = apsp_detail_launch_status();
+  (void)hipFreeAsync(edges, s);
+  return st_launch;
 }
 
 }  // namespace

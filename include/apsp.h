@@ -242,7 +242,11 @@ int apsp_fw_host_plan(int64_t n, int64_t elem_bytes, int64_t device_bytes, int64
  * Pointers 4-byte aligned (128-bit loads when w and d are 16-byte aligned and
  * ldw, ldd are multiples of 4).  Following nxt from i reaches j along a path
  * whose weights sum to d[i][j] when every weight on it is positive.
- * Asynchronous on `stream`; allocates nothing.  Errors as for apsp_fw_i32.
+ * Work: n^3 candidates when w has more than n^2/16 finite off-diagonal
+ * entries; else only the neighbours of each i are tried (n candidates per
+ * edge).  The same matrix either way.  Asynchronous on `stream` (the choice
+ * is made on the device); uses 8 bytes of stream-ordered scratch.  Errors as
+ * for apsp_fw_i32.
  */
 int apsp_successors_i32(const int32_t *w, int64_t ldw, const int32_t *d, int64_t ldd,
                         int32_t *nxt, int64_t ldn, int64_t n, int32_t inf, void *stream);

@@ -58,6 +58,46 @@ def test_int32_successors_match_oracle(dev, orc, n):
     assert np.array_equal(got, orc.successors(w, d, INF))
 
 
+# The call picks one of two kernels from the number of finite off-diagonal
+# weights: a neighbour-list kernel up to n^2 / 16, the dense product above.
+# Both compute the same matrix; these cases sit on either side.
+
+@pytest.mark.parametrize("n", [129, 1000])
+def test_int32_successors_dense_side(dev, orc, n):
+    print(f"case successors i32 dense side n={n}", flush=True)
+    w = tie_graph(n, 0.12, 900 + n)
+    assert ((w < INF).sum() - n) > n * n // 16
+    d = orc.fw_i32(w)
+    assert np.array_equal(gpu_successors(dev, w, d), orc.successors(w, d, INF))
+
+
+def test_int32_successors_hub_rows_take_several_gathers(dev, orc):
+    # rows with more neighbours than one gather holds (2048), in a sparse matrix
+    print("case successors i32 hub rows n=2500", flush=True)
+    n = 2500
+    w = tie_graph(n, 0.004, 31)
+    rng = np.random.default_rng(5)
+    for r in (0, 1, 1234, n - 1):
+        w[r, :] = rng.integers(1, 4, size=n)
+        w[r, r] = 0
+    assert ((w < INF).sum() - n) <= n * n // 16
+    d = orc.fw_i32(w)
+    assert np.array_equal(gpu_successors(dev, w, d), orc.successors(w, d, INF))
+
+
+@pytest.mark.parametrize("p", [0.02, 0.2])
+def test_float32_successors_exact_on_integer_weights(dev, orc, p):
+    # small integer weights are exact in binary32, so both kernels must give
+    # the oracle's int32 matrix
+    print(f"case successors f32 integer weights p={p}", flush=True)
+    n = 500
+    w = tie_graph(n, p, 77)
+    d = orc.fw_i32(w)
+    wf = np.where(w == INF, np.inf, w).astype(np.float32)
+    df = np.where(d == INF, np.inf, d).astype(np.float32)
+    assert np.array_equal(gpu_successors(dev, wf, df), orc.successors(w, d, INF))
+
+
 def test_grid_successors_and_paths(dev, orc):
     print("case successors grid", flush=True)
     w = gg.grid(24, 30)
