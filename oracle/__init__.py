@@ -226,7 +226,9 @@ class Oracle:
 
     def successors(self, w, d, inf):
         """First-hop matrix (int32) of weights w and distances d (both n x n
-        integer arrays): smallest u != i minimising w[i][u] + d[u][j]."""
+        integer arrays): smallest u != i minimising w[i][u] + d[u][j] over
+        the candidates below inf; -1 when there is none (j unreachable, as a
+        distance that is not below inf is), i on the diagonal."""
         ww = np.ascontiguousarray(w, dtype=np.int64)
         dd = np.ascontiguousarray(d, dtype=np.int64)
         n = ww.shape[0]

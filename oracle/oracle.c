@@ -352,6 +352,7 @@ void oracle_successors_i64(const int64_t *w, const int64_t *d, int32_t *nxt, int
       for (int64_t u = 0; u < n; ++u) {
         if (u == i || w[i * ld + u] == inf || d[u * ld + j] == inf) continue;
         const int64_t cand = w[i * ld + u] + d[u * ld + j];
+        if (cand >= inf) continue;  /* not below the sentinel: no path, as for the distances */
         if (arg < 0 || cand < best) { best = cand; arg = u; }
       }
       nxt[i * ld + j] = (int32_t)arg;

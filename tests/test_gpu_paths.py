@@ -25,7 +25,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_successors(dev, w, d, ldn=None, offset=0):
+def gpu_successors(dev, w, d, ldn=None, offset=0, inf=None):
     n = w.shape[0]
     ldn = n if ldn is None else ldn
     tw = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
@@ -34,7 +34,8 @@ def gpu_successors(dev, w, d, ldn=None, offset=0):
     out = buf[offset:offset + n * ldn].view(n, ldn)
     s = torch.cuda.current_stream().cuda_stream
     fn = ga.apsp_successors_i32 if w.dtype == np.int32 else ga.apsp_successors_f32
-    inf = INF if w.dtype == np.int32 else float("inf")
+    if inf is None:
+        inf = INF if w.dtype == np.int32 else float("inf")
     st = fn(tw.data_ptr(), n, td.data_ptr(), n, out.data_ptr(), ldn, n, inf, s)
     assert st == ga.APSP_OK, ga.apsp_status_string(st)
     host = buf.cpu().numpy()
@@ -96,6 +97,20 @@ def test_float32_successors_exact_on_integer_weights(dev, orc, p):
     wf = np.where(w == INF, np.inf, w).astype(np.float32)
     df = np.where(d == INF, np.inf, d).astype(np.float32)
     assert np.array_equal(gpu_successors(dev, wf, df), orc.successors(w, d, INF))
+
+
+@pytest.mark.parametrize("n,p", [(64, 0.02), (64, 0.5)])
+def test_int32_successors_small_sentinel(dev, orc, n, p):
+    # inf = 10 with weights 4..6: two-hop sums already reach the sentinel, and
+    # a pair whose every path sum is >= inf has no first hop (as its distance
+    # is inf); sparse (p = 0.02) and dense (p = 0.5) kernels
+    print(f"case successors small sentinel n={n} p={p}", flush=True)
+    inf = 10
+    w = gg.erdos_renyi(n, p, 4, 6, 40 + int(p * 100), inf=inf)
+    d = orc.fw_i32(w)
+    want = orc.successors(w, d, inf)
+    assert (want == -1).any() and (d == inf).any()
+    assert np.array_equal(gpu_successors(dev, w, d, inf=inf), want)
 
 
 def test_grid_successors_and_paths(dev, orc):

@@ -64,6 +64,7 @@ MUTANTS = {
                          "if (arg < 0 || cand <= best) { best = cand; arg = u; }"),
     "succ_self_allowed": ("if (u == i || w[i * ld + u] == inf || d[u * ld + j] == inf) continue;",
                           "if (w[i * ld + u] == inf || d[u * ld + j] == inf) continue;"),
+    "succ_sentinel_sum_accepted": ("        if (cand >= inf) continue;", ""),
     # min-plus product
     "mp_transposed_b": ("const int64_t btj = b[t * ldb + j];", "const int64_t btj = b[j * ldb + t];"),
     "mp_ignores_c": ("        if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;\n      }\n    }\n}\n\nvoid oracle_minplus_f64",
@@ -182,6 +183,8 @@ def _battery_successors(o: oracle.Oracle) -> None:
     w = gg.grid(4, 5)
     nxt = o.successors(w, o.fw_i32(w), INF)
     assert nxt[19, 0] == 14 and nxt[0, 19] == 1 and nxt[7, 7] == 7
+    w3 = np.array([[0, 6, 10], [10, 0, 6], [10, 10, 0]], dtype=np.int32)
+    assert o.successors(w3, o.fw_i32(w3), 10)[0, 2] == -1
 
 
 def _build_variant(tmp_path, name, edit):

@@ -496,6 +496,17 @@ def test_successors_hand_example(orc):
     assert np.array_equal(got, g["successors"])
 
 
+def test_successors_sum_reaching_the_sentinel_is_unreachable(orc):
+    # inf = 10: 0 -> 1 -> 2 weighs 12, so d(0, 2) stays at the sentinel and
+    # 2 is unreachable from 0 in the sentinel's sense; no first hop either
+    inf = 10
+    w = np.array([[0, 6, inf], [inf, 0, 6], [inf, inf, 0]], dtype=np.int32)
+    d = orc.fw_i32(w)
+    assert d[0, 2] == inf and d[0, 1] == 6 and d[1, 2] == 6
+    nxt = orc.successors(w, d, inf)
+    assert nxt.tolist() == [[0, 1, -1], [-1, 1, 2], [-1, -1, 2]]
+
+
 def all_shortest_first_hops(w, inf):
     """Brute force: the set of first vertices over every shortest simple
     path i -> j (n <= 7)."""
