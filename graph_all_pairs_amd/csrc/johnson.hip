@@ -304,18 +304,34 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
     for (;;) {
       // -- remove ---------------------------------------------------------
       uint32_t lmin = kUnreached;
-      for (int32_t x = tid; x < nw; x += kSsspThreads) {
-        const uint32_t bits = mark[x];
-        if (bits == 0) continue;
-        uint32_t take = 0;
-        for (uint32_t b = bits; b; b &= b - 1) {
-          const int i = __builtin_ctz(b);
-          const uint32_t dv = dist[x * 32 + i];
-          if (dv <= T) take |= 1u << i;
-          else lmin = min(lmin, dv);
+      // Queue slots are claimed once per wave (a scan over the lanes' counts
+      // and one LDS atomic), not once per mark word.
+      for (int32_t x0 = 0; x0 < nw; x0 += kSsspThreads) {
+        const int32_t x = x0 + tid;
+        uint32_t bits = 0, take = 0;
+        if (x < nw) {
+          bits = mark[x];
+          for (uint32_t b = bits; b; b &= b - 1) {
+            const int i = __builtin_ctz(b);
+            const uint32_t dv = dist[x * 32 + i];
+            if (dv <= T) take |= 1u << i;
+            else lmin = min(lmin, dv);
+          }
         }
+        const uint32_t c = (uint32_t)__builtin_popcount(take);
+        uint32_t incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
+          if (lane >= o) incl += y;
+        }
+        const uint32_t wtot = (uint32_t)__shfl((int)incl, 63);
+        if (wtot == 0) continue;
+        uint32_t wbase = 0;
+        if (lane == 63) wbase = atomicAdd(&ctl[par][0], wtot);
+        wbase = (uint32_t)__shfl((int)wbase, 63);
         if (take == 0) continue;
-        const uint32_t base = atomicAdd(&ctl[par][0], (uint32_t)__builtin_popcount(take));
+        const uint32_t base = wbase + incl - c;
         if (base >= (uint32_t)qcap) continue;
         uint32_t k = base, kept = 0;
         for (uint32_t b = take; b && k < (uint32_t)qcap; b &= b - 1) {
