@@ -69,6 +69,9 @@ constexpr int kHubUnroll = APSP_JO_HUB_UNROLL;  // edge loads in flight per lane
 #ifndef APSP_JO_G
 #define APSP_JO_G 0           // lanes per edge chunk; 0 = by average degree
 #endif
+#ifndef APSP_JO_FORCE_GD
+#define APSP_JO_FORCE_GD 0    // 1: distances in global memory even when the row fits LDS
+#endif
 #ifndef APSP_JO_WG_PER_CU
 #define APSP_JO_WG_PER_CU 0   // search workgroups per CU; 0 = as many as LDS allows (<= 2)
 #endif
@@ -246,7 +249,14 @@ __global__ void __launch_bounds__(256) jo_reweight(const int64_t* __restrict__ r
 // workgroups share a CU; wider unrolling of the hub loop crossed that limit
 // and halved the throughput.
 // ---------------------------------------------------------------------------
-template <int G>
+//
+// GD (a row too long for LDS): the tentative distances live in the source's
+// own output row in global memory instead, reinterpreted as uint32 until
+// the row is transformed back.  Only this workgroup touches that row; its
+// reads are L2-coherent atomic loads (an L1 line could be stale after
+// another wave's L2 atomic) and its updates L2 atomics.  The bitmap and the
+// queue stay in LDS.
+template <int G, bool GD>
 __global__ void __launch_bounds__(kSsspThreads) __attribute__((amdgpu_waves_per_eu(4)))
 jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_t n,
          const int32_t* __restrict__ h32, int32_t* __restrict__ d, int64_t ld, int32_t inf,
@@ -255,8 +265,8 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
   const int32_t n4 = (n + 3) & ~3;
   const int32_t nw = (n + 31) >> 5;
   const int32_t nw4 = (nw + 3) & ~3;
-  uint32_t* dist = smem;
-  uint32_t* mark = dist + n4;
+  uint32_t* dist = smem;  // GD: set to the source's row below
+  uint32_t* mark = smem + (GD ? 0 : n4);
   uint32_t* qv = mark + nw4;
   uint32_t* qs = qv + qcap;
   uint32_t* qe = qs + qcap;
@@ -272,11 +282,19 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
   int32_t err = 0;
   unsigned long long n_steps = 0, n_removed = 0, n_edges = 0;
 
+  auto dget = [&](uint32_t v) -> uint32_t {
+    if constexpr (GD) return __hip_atomic_load(&dist[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return dist[v];
+  };
+  auto dset = [&](uint32_t v, uint32_t x) {
+    if constexpr (GD) __hip_atomic_store(&dist[v], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else dist[v] = x;
+  };
   auto relax = [&](uint32_t du, int2 x) {
     const uint32_t v = (uint32_t)x.x;
     uint32_t nd = du + (uint32_t)x.y;
     if (nd < du) nd = kUnreached;  // saturate instead of wrapping
-    if (nd < dist[v]) {
+    if (nd < dget(v)) {
       const uint32_t old = atomicMin(&dist[v], nd);
       if (nd < old) atomicOr(&mark[v >> 5], 1u << (v & 31));
     }
@@ -287,13 +305,14 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
     __syncthreads();
     const int32_t s = s_src;
     if (s >= n) break;
+    if constexpr (GD) dist = reinterpret_cast<uint32_t*>(d + (int64_t)s * ld);
 
-    for (int32_t v = tid; v < n; v += kSsspThreads) dist[v] = kUnreached;
+    for (int32_t v = tid; v < n; v += kSsspThreads) dset(v, kUnreached);
     for (int32_t x = tid; x < nw; x += kSsspThreads) mark[x] = 0;
     if (tid < 8) ctl[tid >> 2][tid & 3] = (tid & 3) == 1 ? kUnreached : 0u;
     __syncthreads();
     if (tid == 0) {
-      dist[s] = 0;
+      dset(s, 0);
       mark[s >> 5] = 1u << (s & 31);
     }
     __syncthreads();
@@ -313,7 +332,7 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
           bits = mark[x];
           for (uint32_t b = bits; b; b &= b - 1) {
             const int i = __builtin_ctz(b);
-            const uint32_t dv = dist[x * 32 + i];
+            const uint32_t dv = dget(x * 32 + i);
             if (dv <= T) take |= 1u << i;
             else lmin = min(lmin, dv);
           }
@@ -407,7 +426,7 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
             a = qs[i];
             b = qe[i];
             if (b - a > kBig) b = a;  // a hub: relaxed below
-            du[m] = dist[qv[i]];
+            du[m] = dget(qv[i]);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -426,7 +445,7 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
       for (uint32_t h = (uint32_t)(tid >> 6); h < nbig; h += kSsspWaves) {
         const uint32_t i = big[h];
         const uint32_t a = qs[i], b = qe[i];
-        const uint32_t du = dist[qv[i]];
+        const uint32_t du = dget(qv[i]);
         for (uint32_t e0 = a + (uint32_t)lane; e0 < b; e0 += kHubUnroll * 64) {
           int2 x[kHubUnroll];
           bool ok[kHubUnroll];
@@ -447,7 +466,7 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
     const int64_t hs = h32[s];
     int32_t* row = d + (int64_t)s * ld;
     for (int32_t v = tid; v < n; v += kSsspThreads) {
-      const uint32_t dv = dist[v];
+      const uint32_t dv = dget(v);  // GD: the same word as row[v], read before it is written
       int32_t out = inf;
       if (dv != kUnreached) {
         const int64_t x = (int64_t)dv + (int64_t)h32[v] - hs;
@@ -504,13 +523,18 @@ int hip_failed() {
 template <int G>
 int launch_sssp(const int64_t* row_ptr, const int2* ew, int32_t n, const int32_t* h32, int32_t* d,
                 int64_t ld, int32_t inf, uint32_t delta, int32_t qcap, size_t lds, int grid,
-                Stats* st, hipStream_t s) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&jo_sssp<G>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+                bool gd, Stats* st, hipStream_t s) {
+  const void* fn = gd ? reinterpret_cast<const void*>(&jo_sssp<G, true>)
+                      : reinterpret_cast<const void*>(&jo_sssp<G, false>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return hip_failed();
   const int64_t step_cap = 64 * (int64_t)n + 4096;
-  hipLaunchKernelGGL((jo_sssp<G>), dim3(grid), dim3(kSsspThreads), lds, s, row_ptr, ew, n, h32, d,
-                     ld, inf, delta, qcap, step_cap, st);
+  if (gd)
+    hipLaunchKernelGGL((jo_sssp<G, true>), dim3(grid), dim3(kSsspThreads), lds, s, row_ptr, ew, n, h32,
+                       d, ld, inf, delta, qcap, step_cap, st);
+  else
+    hipLaunchKernelGGL((jo_sssp<G, false>), dim3(grid), dim3(kSsspThreads), lds, s, row_ptr, ew, n,
+                       h32, d, ld, inf, delta, qcap, step_cap, st);
   return apsp_detail_launch_status();
 }
 
@@ -548,21 +572,26 @@ int run_johnson(const int64_t* row_ptr, const int32_t* col, const int32_t* w, in
   if (st != APSP_OK) return st;
   const int64_t n4 = (n + 3) & ~int64_t(3);
   const int64_t nw4 = (((n + 31) >> 5) + 3) & ~int64_t(3);
-  const int64_t fixed = 4 * (n4 + nw4) + 1024;  // + static LDS and slack
   int32_t qcap = 0;
   int per_cu = 0;
+  bool gd = false;
   // Two 512-thread search workgroups fit a CU by registers (four waves per
-  // SIMD); LDS decides between two and one.
-  for (int k = APSP_JO_WG_PER_CU ? APSP_JO_WG_PER_CU : 2; k >= 1 && qcap == 0; k /= 2) {
-    const int64_t budget = std::min<int64_t>(lds_cu / k, lds_block);
-    const int64_t q = std::min<int64_t>(kMaxQcap, (budget - fixed) / 16) & ~int64_t(63);
-    if (q >= 256 || (k == 1 && q >= 64)) {
-      qcap = (int32_t)q;
-      per_cu = k;
+  // SIMD); LDS decides between two and one.  A row that does not fit at all
+  // moves to global memory (GD), leaving the bitmap and the queue in LDS.
+  for (int pass = APSP_JO_FORCE_GD; pass < 2 && qcap == 0; ++pass) {
+    gd = pass == 1;
+    const int64_t fixed = 4 * ((gd ? 0 : n4) + nw4) + 1024;  // + static LDS and slack
+    for (int k = APSP_JO_WG_PER_CU ? APSP_JO_WG_PER_CU : 2; k >= 1 && qcap == 0; k /= 2) {
+      const int64_t budget = std::min<int64_t>(lds_cu / k, lds_block);
+      const int64_t q = std::min<int64_t>(kMaxQcap, (budget - fixed) / 16) & ~int64_t(63);
+      if (q >= 256 || (k == 1 && q >= 64)) {
+        qcap = (int32_t)q;
+        per_cu = k;
+      }
     }
   }
-  if (qcap == 0) return APSP_ERR_RANGE;  // the row does not fit in one workgroup's LDS
-  const size_t lds = (size_t)(4 * (n4 + nw4 + 4 * (int64_t)qcap));
+  if (qcap == 0) return APSP_ERR_RANGE;  // not even the bitmap fits in one workgroup's LDS
+  const size_t lds = (size_t)(4 * ((gd ? 0 : n4) + nw4 + 4 * (int64_t)qcap));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t off_stats = 0;
@@ -679,15 +708,15 @@ int run_johnson(const int64_t* row_ptr, const int32_t* col, const int32_t* w, in
                      : avg_deg <= 128.0 ? 32
                                         : 64;
     if (gsel == 4)
-      rc = launch_sssp<4>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, dst, s);
+      rc = launch_sssp<4>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, gd, dst, s);
     else if (gsel == 8)
-      rc = launch_sssp<8>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, dst, s);
+      rc = launch_sssp<8>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, gd, dst, s);
     else if (gsel == 16)
-      rc = launch_sssp<16>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, dst, s);
+      rc = launch_sssp<16>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, gd, dst, s);
     else if (gsel == 32)
-      rc = launch_sssp<32>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, dst, s);
+      rc = launch_sssp<32>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, gd, dst, s);
     else
-      rc = launch_sssp<64>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, dst, s);
+      rc = launch_sssp<64>(row_ptr, ew, (int32_t)n, h32, d, ld, inf, dl, qcap, lds, grid, gd, dst, s);
     mark(7);
     if (rc != APSP_OK) break;
     if ((rc = sync_read(s, &hs, dst, sizeof(Stats))) != APSP_OK) break;

@@ -48,6 +48,7 @@ __all__ = [
     "two_rings", "WORKLOADS", "make_workload", "sha256_matrix", "pad_ld",
     "erdos_renyi_batch", "complete_f32_batch", "BATCH_WORKLOADS", "make_batch_workload",
     "erdos_renyi_potential", "csr_from_dense", "JOHNSON_WORKLOADS", "make_johnson_workload",
+    "regular_out_csr",
 ]
 
 INF_I32 = 0x3FFFFFFF          # the int32 "no edge" sentinel of the workloads
@@ -392,6 +393,31 @@ def erdos_renyi_potential(n: int, p: float, wlo: int, whi: int, plo: int, phi: i
     blk = np.where(edge, blk + pot[:, None] - pot[None, :], blk)
     m[:, :n] = blk.astype(np.int32)
     return m
+
+
+def regular_out_csr(n: int, deg: int, wlo: int, whi: int, seed: int, plo: int = 0,
+                    phi: int = 0):
+    """A sparse digraph built straight in CSR form (no dense matrix), for
+    vertex counts whose n x n matrix would not fit the host: every vertex u
+    has ``deg`` out-edges to targets u + 1 + (r mod (n - 1)) (mod n), r drawn
+    per edge, so never u itself (parallel edges may occur).  Weights w0 are
+    uniform on [wlo, whi]; with phi > plo every edge is shifted by vertex
+    potentials p uniform on [plo, phi]: w = w0 + p(u) - p(v), which leaves
+    every cycle's weight unchanged (no negative cycle when w0 >= 0).
+    Returns (row_ptr int64 [n+1], col int32 [n*deg], w int32 [n*deg])."""
+    if n < 2:
+        raise ValueError("needs n >= 2")
+    m = n * deg
+    e = np.arange(m, dtype=np.uint64)
+    u = (np.arange(m, dtype=np.int64) // deg)
+    r = (u64_array(seed, _S_EDGE, e) >> np.uint64(1)) % np.uint64(n - 1)
+    col = ((u + 1 + r.astype(np.int64)) % n).astype(np.int32)
+    w = _uniform_int(u64_array(seed, _S_WEIGHT, e), wlo, whi)
+    if phi > plo:
+        pot = _uniform_int(u64_array(seed, _S_POTENTIAL, np.arange(n, dtype=np.uint64)), plo, phi)
+        w = w + pot[u] - pot[col]
+    row_ptr = np.arange(n + 1, dtype=np.int64) * deg
+    return row_ptr, col, w.astype(np.int32)
 
 
 def csr_from_dense(m: np.ndarray, inf, n: int | None = None):

@@ -362,9 +362,11 @@ int apsp_fw_batched_f32(float *d, int64_t batch, int64_t n, int64_t ld, int64_t 
  * Synchronous: the call reads device results between its steps and returns
  * after all of its work on `stream` has completed.  It takes stream-ordered
  * scratch (hipMallocAsync on `stream`) of about 14n + 8nnz bytes and frees
- * it before returning.  The row of each source lives in one workgroup's
- * LDS (4n bytes plus a small queue), which bounds n to about 38 000 on
- * gfx950; a larger n returns APSP_ERR_RANGE before any work.
+ * it before returning.  The tentative distances of each source live in one
+ * workgroup's LDS (4n bytes plus a small queue) up to n of about 38 000 on
+ * gfx950; beyond that they live in the source's own row of d in global
+ * memory (slower), with a bitmap of n/8 bytes and the queue still in LDS,
+ * which bounds n to about 1.2 million (else APSP_ERR_RANGE before any work).
  * Other errors as for apsp_fw_i32.
  */
 int apsp_johnson_i32(const int64_t *row_ptr, const int32_t *col, const int32_t *w,

@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 
 import graphgen as gg
+import oracle
 
 
 def test_counter_rng_scalar_matches_vector():
@@ -112,3 +113,48 @@ def test_batch_workload_table():
     for name, w in gg.BATCH_WORKLOADS.items():
         assert name.startswith("batch-") and w["n"] <= 128 and w["batch"] >= 1
         assert w["dtype"] in name
+
+
+def test_regular_out_csr_structure():
+    n, deg = 1000, 5
+    rp, col, w = gg.regular_out_csr(n, deg, 3, 9, 17)
+    assert rp.dtype == np.int64 and col.dtype == np.int32 and w.dtype == np.int32
+    assert np.array_equal(rp, np.arange(n + 1) * deg)
+    u = np.repeat(np.arange(n), deg)
+    assert (col != u).all() and col.min() >= 0 and col.max() < n
+    assert w.min() >= 3 and w.max() <= 9
+    # deterministic, and a different seed gives a different graph
+    rp2, col2, w2 = gg.regular_out_csr(n, deg, 3, 9, 17)
+    assert np.array_equal(col, col2) and np.array_equal(w, w2)
+    assert not np.array_equal(col, gg.regular_out_csr(n, deg, 3, 9, 18)[1])
+
+
+def test_regular_out_csr_potentials_keep_cycle_weights():
+    # w = w0 + p(u) - p(v): the shift telescopes around any cycle, so the
+    # shifted graph's distances are the unshifted ones plus p(s) - p(t)
+    n, deg = 300, 4
+    rp, col, w0 = gg.regular_out_csr(n, deg, 0, 50, 5)
+    _, col1, w = gg.regular_out_csr(n, deg, 0, 50, 5, -40, 40)
+    assert np.array_equal(col, col1) and (w < 0).any()
+    o = oracle.default()
+    src = [0, 7, 299]
+    d0, neg0 = o.bf_rows_csr(rp, col, w0, n, src, gg.INF_I32)
+    d1, neg1 = o.bf_rows_csr(rp, col, w, n, src, gg.INF_I32)
+    assert not neg0.any() and not neg1.any()
+    shift = (w.astype(np.int64) - w0)                      # p(u) - p(v) per edge
+    p = np.zeros(n, dtype=np.int64)                        # recover p up to a constant along BFS
+    seen = np.zeros(n, dtype=bool)
+    seen[0] = True
+    stack = [0]
+    while stack:
+        u = stack.pop()
+        for e in range(rp[u], rp[u + 1]):
+            v = col[e]
+            if not seen[v]:
+                p[v] = p[u] - shift[e]
+                seen[v] = True
+                stack.append(v)
+    reach = d0 < gg.INF_I32
+    for k, s in enumerate(src):
+        both = reach[k] & seen
+        assert np.array_equal((d1[k] - d0[k])[both], (p[s] - p)[both])
