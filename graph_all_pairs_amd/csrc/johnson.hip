@@ -59,7 +59,11 @@ namespace {
 
 constexpr int kSsspThreads = 512;           // per-source search workgroup
 constexpr int kSsspWaves = kSsspThreads / 64;
-constexpr int kMaxQcap = 4 * kSsspThreads;  // queue entries (edge ranges: <= 4 per thread)
+#ifndef APSP_JO_MAX_QCAP
+#define APSP_JO_MAX_QCAP 4096
+#endif
+constexpr int kMaxQcap = APSP_JO_MAX_QCAP;  // queue entries
+constexpr int kQueueBytes = 6;              // LDS per queue entry: vertex + half a hub slot
 constexpr uint32_t kUnreached = 0xFFFFFFFFu;
 constexpr int kBfRoundsPerCheck = 8;
 #ifndef APSP_JO_HUB_UNROLL
@@ -231,20 +235,22 @@ __global__ void __launch_bounds__(256) jo_reweight(const int64_t* __restrict__ r
 }
 
 // ---------------------------------------------------------------------------
-// Per-source search (steps 3 and 4).  A step is remove -> edge ranges ->
-// relax, with a barrier after each:
+// Per-source search (steps 3 and 4).  A step is remove -> relax -> hubs,
+// with a barrier after each:
 //   remove   marked vertices with distance <= T leave the bitmap for the
 //            queue (at most qcap per step; the rest stay marked);
-//   ranges   each queued vertex's adjacency [row_ptr[u], row_ptr[u+1]) is
-//            fetched, all queue entries at once;
-//   relax    each group of G lanes relaxes whole adjacencies of up to 4G
-//            edges, two at a time (up to 8 edge loads in flight per lane);
-//            longer adjacencies (hubs) go to one wave each, the waves in
-//            parallel.
+//   relax    each group of G lanes fetches the adjacency [row_ptr[u],
+//            row_ptr[u+1]) of a queued vertex and relaxes it whole when it
+//            has up to 4G edges, two vertices at a time (up to 8 edge loads
+//            in flight per lane); a longer adjacency (a hub) is listed;
+//   hubs     one wave per listed hub, the waves in parallel.
 // Dynamic LDS (32-bit words): dist[n4] tentative distances (kUnreached = not
 // reached), mark[nw4] the bitmap of vertices whose distance dropped since
-// they were last removed, and qv, qs, qe, big [qcap each]: queued vertex,
-// its first and end edge, and the queue positions of the hubs.
+// they were last removed, qv[qcap] the queued vertices and big[qcap / 2]
+// the queue positions of the hubs.  With the list full, a hub's group
+// relaxes the rest of it.  Fetching the ranges inside the relax loop
+// instead of in a phase of their own keeps the queue at 6 bytes per entry,
+// so more vertices fit a step (BA-16000: 38 steps per source instead of 48).
 // Held to four waves per SIMD (<= 128 VGPRs) so that two 512-thread
 // workgroups share a CU; wider unrolling of the hub loop crossed that limit
 // and halved the throughput.
@@ -268,9 +274,8 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
   uint32_t* dist = smem;  // GD: set to the source's row below
   uint32_t* mark = smem + (GD ? 0 : n4);
   uint32_t* qv = mark + nw4;
-  uint32_t* qs = qv + qcap;
-  uint32_t* qe = qs + qcap;
-  uint32_t* big = qe + qcap;
+  uint32_t* big = qv + qcap;
+  const uint32_t hcap = (uint32_t)qcap / 2;
   __shared__ uint32_t ctl[2][4];  // per step parity: queue count, smallest marked distance > T, hubs
   __shared__ int32_t s_src;
   constexpr uint32_t kBig = 4 * G;
@@ -386,47 +391,37 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
         continue;
       }
 
-      // -- edge ranges of the removed vertices (loads issued together) -------
-      {
-        uint32_t a[4], b[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t i = tid + k * kSsspThreads;
-          if (i < qn) {
-            const uint32_t u = qv[i];
-            a[k] = (uint32_t)row_ptr[u];
-            b[k] = (uint32_t)row_ptr[u + 1];
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t i = tid + k * kSsspThreads;
-          if (i < qn) {
-            qs[i] = a[k];
-            qe[i] = b[k];
-            n_edges += b[k] - a[k];
-            if (b[k] - a[k] > kBig) big[atomicAdd(&ctl[par][2], 1u)] = i;
-          }
-        }
-      }
-      __syncthreads();
-      const uint32_t nbig = ctl[par][2];
-      par ^= 1;
-
-      // -- relax: short adjacencies per group, two at a time ------------------
+      // -- relax: each group fetches its vertices' edge ranges itself --------
+      // A hub (more than 4G edges) goes to the hub list for a whole wave;
+      // when the list is full, its group relaxes the rest of it in strides.
       for (uint32_t i0 = grp; i0 < qn; i0 += 2 * kGroups) {
         int2 x[2][4];
-        uint32_t du[2];
+        uint32_t du[2], rest_a[2], rest_b[2];
         bool ok[2][4];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const uint32_t i = i0 + m * kGroups;
           uint32_t a = 0, b = 0;
+          rest_a[m] = rest_b[m] = 0;
           if (i < qn) {
-            a = qs[i];
-            b = qe[i];
-            if (b - a > kBig) b = a;  // a hub: relaxed below
-            du[m] = dget(qv[i]);
+            const uint32_t u = qv[i];
+            a = (uint32_t)row_ptr[u];
+            b = (uint32_t)row_ptr[u + 1];
+            if (gl == 0) n_edges += b - a;
+            if (b - a > kBig) {
+              uint32_t slot = 0;
+              if (gl == 0) slot = atomicAdd(&ctl[par][2], 1u);
+              slot = (uint32_t)__shfl((int)slot, lane - (int)gl);
+              if (slot < hcap) {
+                if (gl == 0) big[slot] = i;
+                b = a;  // relaxed by a wave below
+              } else {
+                rest_a[m] = a + kBig;
+                rest_b[m] = b;
+                b = a + kBig;
+              }
+            }
+            du[m] = dget(u);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -440,12 +435,18 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (ok[m][j]) relax(du[m], x[m][j]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          for (uint32_t e = rest_a[m] + gl; e < rest_b[m]; e += G) relax(du[m], ew[e]);
       }
+      __syncthreads();
+      const uint32_t nbig = min(ctl[par][2], hcap);
+      par ^= 1;
       // -- hubs: one wave per long adjacency, the waves in parallel -----------
       for (uint32_t h = (uint32_t)(tid >> 6); h < nbig; h += kSsspWaves) {
-        const uint32_t i = big[h];
-        const uint32_t a = qs[i], b = qe[i];
-        const uint32_t du = dget(qv[i]);
+        const uint32_t u = qv[big[h]];
+        const uint32_t a = (uint32_t)row_ptr[u], b = (uint32_t)row_ptr[u + 1];
+        const uint32_t du = dget(u);
         for (uint32_t e0 = a + (uint32_t)lane; e0 < b; e0 += kHubUnroll * 64) {
           int2 x[kHubUnroll];
           bool ok[kHubUnroll];
@@ -583,7 +584,7 @@ int run_johnson(const int64_t* row_ptr, const int32_t* col, const int32_t* w, in
     const int64_t fixed = 4 * ((gd ? 0 : n4) + nw4) + 1024;  // + static LDS and slack
     for (int k = APSP_JO_WG_PER_CU ? APSP_JO_WG_PER_CU : 2; k >= 1 && qcap == 0; k /= 2) {
       const int64_t budget = std::min<int64_t>(lds_cu / k, lds_block);
-      const int64_t q = std::min<int64_t>(kMaxQcap, (budget - fixed) / 16) & ~int64_t(63);
+      const int64_t q = std::min<int64_t>(kMaxQcap, (budget - fixed) / kQueueBytes) & ~int64_t(63);
       if (q >= 256 || (k == 1 && q >= 64)) {
         qcap = (int32_t)q;
         per_cu = k;
@@ -591,7 +592,7 @@ int run_johnson(const int64_t* row_ptr, const int32_t* col, const int32_t* w, in
     }
   }
   if (qcap == 0) return APSP_ERR_RANGE;  // not even the bitmap fits in one workgroup's LDS
-  const size_t lds = (size_t)(4 * ((gd ? 0 : n4) + nw4 + 4 * (int64_t)qcap));
+  const size_t lds = (size_t)(4 * ((gd ? 0 : n4) + nw4) + (int64_t)kQueueBytes * qcap);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t off_stats = 0;
