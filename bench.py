@@ -21,6 +21,10 @@ batch; value = batch * n^3 / (wall time per step), and the roofline entry
 describes the batched kernel (one launch per step, timed with events on its
 stream).
 
+With --workload shard-<workload>-p<P> a step is one GPU's share of one round's
+Phase 3 when the matrix is split into P block rows (the multi-GPU design): the
+(n/P) x n slab updated through apsp_minplus_gemm; value = its relaxations/s.
+
 With --workload johnson-... (sparse graphs, see graphgen.JOHNSON_WORKLOADS) a
 step is one apsp_johnson_timed_i32 call (CSR on the device, dense n x n
 distances out); value = n^3 / (wall time per step), the rate a dense
@@ -546,6 +550,118 @@ def bench_host(args) -> int:
     return 0
 
 
+def parse_shard(name: str):
+    """shard-<workload>-p<P> -> (workload, P), else None."""
+    m = re.fullmatch(r"shard-(.+)-p(\d+)", name)
+    return (m.group(1), int(m.group(2))) if m else None
+
+
+def bench_shard(args) -> int:
+    """One GPU's share of one round's Phase 3 when the matrix is split into P
+    block rows, one per GPU: the (n/P) x n slab takes C <- min(C, A (x) B)
+    with A its n/P x B pivot columns and B the B x n pivot-row panel that
+    the owner of block row K broadcasts.  It runs through apsp_minplus_gemm
+    (the Phase-3 register tiling, C resident for the whole depth) at that
+    shape, on the workload's values, in the arithmetic the in-core call
+    uses (binary32 for an int32 matrix whose entries are exact there).  A
+    step is one slab update, timed with HIP events on its stream."""
+    import numpy as np
+    import torch
+
+    import graph_all_pairs_amd as ga
+    import graphgen as gg
+
+    base, P = parse_shard(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gg.make_workload(base)
+    n = w.shape[0]
+    B = ga.apsp_pivot_block(n)
+    nb = (n + B - 1) // B
+    if P < 1 or n % P or (n // P) % B:
+        raise SystemExit(f"bench.py: {n} rows do not split into {P} block rows of whole pivot blocks")
+    rows = n // P
+    K = nb // 2  # a middle round; the kernel's work does not depend on the values
+    f32 = w.dtype != np.int32 or (
+        bool(((w == gg.INF_I32) | ((w >= 0) & (w <= 1 << 24))).all()))
+    if w.dtype == np.int32 and f32:
+        wf = np.where(w == gg.INF_I32, np.float32(np.inf), w.astype(np.float32))
+    else:
+        wf = w
+    full = torch.from_numpy(np.ascontiguousarray(wf[:, :n]))
+    p = P // 2  # the GPU whose slab is measured
+    c0 = full[p * rows:(p + 1) * rows].to(dev)
+    a = full[p * rows:(p + 1) * rows, K * B:(K + 1) * B].contiguous().to(dev)
+    b = full[K * B:(K + 1) * B].contiguous().to(dev)
+    del full
+    arith = "f32" if c0.dtype == torch.float32 else "int32"
+    steps = max(args.steps, 200)  # a slab update takes tens of microseconds
+    cs = [c0.clone() for _ in range(min(steps + args.warmup, 16))]
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        ga.minplus_gemm(cs[i % len(cs)], a, b)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        ga.minplus_gemm(cs[i % len(cs)], a, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / steps
+    relax = rows * n * B
+    achieved = relax / (ms * 1e-3)
+    peak = PEAK_RELAX[arith]
+    log(f"{args.workload}: slab {rows} x {n}, depth {B} (round {K} of {nb}), {arith}: "
+        f"{ms * 1e3:.1f} us per slab update, {achieved / 1e12:.2f} Trelax/s")
+    # What the other GPUs would wait for: the B x n pivot-row panel on one xGMI link.
+    panel_bytes = B * n * 4
+    roofline = {
+        "bound": "alu", "kernel": "mp_gemm", "achieved": achieved / 1e12,
+        "peak": peak / 1e12, "unit": "Trelax/s", "frac": achieved / peak, "traffic": None,
+        "relax_per_launch": relax, "avg_launch_ms": ms, "launches": steps,
+    }
+    st_c, ceil = ga.apsp_minplus_ceiling(1 if arith == "f32" else 0)
+    if st_c == ga.APSP_OK:
+        roofline["ceiling_measured"] = ceil / 1e12
+        roofline["frac_of_ceiling"] = achieved / ceil
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        sub = rows  # the whole slab: about a second of CPU work
+        ch = c0[:sub].cpu().numpy().astype(np.float64 if arith == "f32" else np.int64)
+        ah = a[:sub].cpu().numpy().astype(ch.dtype)
+        bh = b.cpu().numpy().astype(ch.dtype)
+        t0 = time.perf_counter()
+        if arith == "f32":
+            orc.minplus(ch, ah, bh)
+        else:
+            orc.minplus(ch, ah, bh, gg.INF_I32)
+        dt = time.perf_counter() - t0
+        cpu = {"value": sub * n * B / dt, "unit": "relaxations/s", "cores": orc.threads(),
+               "kind": "oracle",
+               "sample": f"the oracle's min-plus product on {sub} of the {rows} slab rows "
+                         f"({sub * n * B:.3e} relaxations) in {dt:.2f} s"}
+    rec = {
+        "metric": "one GPU's share of one Floyd-Warshall round: slab min-plus update, "
+                  "relaxations/s",
+        "value": achieved, "unit": "relaxations/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "strong", "vs_baseline": None, "dtype": arith, "data": "synthetic",
+        "config": {"workload": args.workload, "matrix": base, "n": n, "gpus_in_design": P,
+                   "slab_rows": rows, "depth": B, "round": K,
+                   "panel_bytes_broadcast": panel_bytes,
+                   "panel_ms_on_one_xgmi_link": panel_bytes / 153e9 * 1e3,
+                   "wall_ms_per_step": 1e3 * wall / steps},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def bench_paths(args) -> int:
     """Distances plus successors: a step is one apsp_fw_i32 call and one
     apsp_successors_i32 call on a dense workload's matrix; the roofline entry
@@ -666,6 +782,9 @@ def main() -> int:
         return bench_host(args)
     if args.workload.startswith("paths-") and args.workload[len("paths-"):] in gg.WORKLOADS:
         return bench_paths(args)
+    shard = parse_shard(args.workload)
+    if shard is not None and shard[0] in gg.WORKLOADS:
+        return bench_shard(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

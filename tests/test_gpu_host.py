@@ -83,6 +83,36 @@ def test_gemm_int32_matches_oracle(dev, m, n, k):
     assert np.array_equal(got.astype(np.int64), oracle.default().minplus(c, a, b, INF))
 
 
+@pytest.fixture(scope="module")
+def share_ops():
+    """One GPU's share of round 32 when complete-8192-i32 is split into 8
+    block rows (GPU 4's slab): C the 1024 x 8192 slab, A its pivot columns,
+    B the round's 128 x 8192 pivot-row panel, and the oracle's product."""
+    w = gg.make_workload("complete-8192-i32")
+    rows, n, B, K, p = 1024, 8192, 128, 32, 4
+    c = np.ascontiguousarray(w[p * rows:(p + 1) * rows, :n])
+    a = np.ascontiguousarray(c[:, K * B:(K + 1) * B])
+    b = np.ascontiguousarray(w[K * B:(K + 1) * B, :n])
+    return c, a, b, oracle.default().minplus(c, a, b, INF)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_gemm_one_gpu_share_of_a_round(dev, share_ops, f32):
+    """The multi-GPU design's per-GPU Phase-3 step at its real shape
+    (bench.py --workload shard-complete-8192-i32-p8 times it).  Bit-exact
+    against the oracle in int32 and in binary32 (integer weights, so every
+    candidate is exact)."""
+    print(f"case one GPU's share, f32={f32}", flush=True)
+    c, a, b, want = share_ops
+    if f32:
+        tf = lambda x: np.where(x == INF, np.float32(np.inf), x.astype(np.float32))
+        got = gpu_gemm(dev, tf(c), tf(a), tf(b))
+        got = np.where(np.isinf(got), INF, got).astype(np.int64)
+    else:
+        got = gpu_gemm(dev, c, a, b).astype(np.int64)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("m,n,k", [(129, 127, 130), (300, 260, 17), (256, 256, 4096)])
 @pytest.mark.parametrize("neg", [False, True])
 def test_gemm_float32_matches_oracle(dev, m, n, k, neg):
