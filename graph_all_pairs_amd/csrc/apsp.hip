@@ -526,9 +526,21 @@ __global__ void __launch_bounds__(kThreads) scan_i32(const int32_t* __restrict__
     }
   };
   const int64_t quads = (n + 3) / 4;
+  const int64_t full = VEC ? n / 4 : 0;  // quads wholly inside the row
   for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
     const int32_t* row = d + r * ld;
-    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+    int64_t q = threadIdx.x;
+    // Four quads in flight per thread before any is visited.
+    for (; q + 3 * kThreads < full; q += 4 * kThreads) {
+      int32_t v[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) load4(row + (q + k * kThreads) * 4, v[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) visit(v[k][e], r, (q + k * kThreads) * 4 + e);
+    }
+    for (; q < quads; q += kThreads) {
       const int64_t c = q * 4;
       if (VEC && c + 3 < n) {
         int32_t v[4];
@@ -579,9 +591,22 @@ __global__ void __launch_bounds__(kThreads) convert_i32(int32_t* __restrict__ d,
     return f32_to_i32(__int_as_float(v), inf);
   };
   const int64_t quads = (n + 3) / 4;
+  const int64_t full = VEC ? n / 4 : 0;  // quads wholly inside the row
   for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
     int32_t* row = d + r * ld;
-    for (int64_t q = threadIdx.x; q < quads; q += kThreads) {
+    int64_t q = threadIdx.x;
+    for (; q + 3 * kThreads < full; q += 4 * kThreads) {  // four quads in flight
+      int32_t v[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) load4(row + (q + k * kThreads) * 4, v[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[k][e] = conv(v[k][e]);
+        store4(row + (q + k * kThreads) * 4, v[k]);
+      }
+    }
+    for (; q < quads; q += kThreads) {
       const int64_t c = q * 4;
       if (VEC && c + 3 < n) {
         int32_t v[4];
