@@ -70,6 +70,9 @@ constexpr int kBfRoundsPerCheck = 8;
 #define APSP_JO_HUB_UNROLL 4
 #endif
 constexpr int kHubUnroll = APSP_JO_HUB_UNROLL;  // edge loads in flight per lane on a hub
+#ifndef APSP_JO_HUB_MUL
+#define APSP_JO_HUB_MUL 8     // a hub has more than APSP_JO_HUB_MUL * G edges
+#endif
 #ifndef APSP_JO_G
 #define APSP_JO_G 0           // lanes per edge chunk; 0 = by average degree
 #endif
@@ -278,7 +281,7 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
   const uint32_t hcap = (uint32_t)qcap / 2;
   __shared__ uint32_t ctl[2][4];  // per step parity: queue count, smallest marked distance > T, hubs
   __shared__ int32_t s_src;
-  constexpr uint32_t kBig = 4 * G;
+  constexpr uint32_t kBig = APSP_JO_HUB_MUL * G;
   constexpr uint32_t kGroups = kSsspThreads / G;
 
   const int tid = threadIdx.x;
@@ -415,11 +418,12 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
               if (slot < hcap) {
                 if (gl == 0) big[slot] = i;
                 b = a;  // relaxed by a wave below
-              } else {
-                rest_a[m] = a + kBig;
-                rest_b[m] = b;
-                b = a + kBig;
               }
+            }
+            if (b - a > 4 * G) {  // the group's four loads per lane, then strides
+              rest_a[m] = a + 4 * G;
+              rest_b[m] = b;
+              b = a + 4 * G;
             }
             du[m] = dget(u);
           }
