@@ -36,7 +36,7 @@
 //    T moves to (smallest marked distance) + delta.  With w' >= 0 the
 //    search ends when nothing is marked, and each distance is then final.
 //  * The edges of the removed vertices are spread over the workgroup by
-//    adjacency length: groups of G lanes take short adjacencies (up to 4G
+//    adjacency length: groups of G lanes take short adjacencies (up to 8G
 //    edges, G from the average degree), whole waves take the long ones.  A
 //    balanced split of all edges by a prefix sum and a per-chunk binary
 //    search was tried first and was 1.3-2.5x slower: its extra barriers and
@@ -244,8 +244,9 @@ __global__ void __launch_bounds__(256) jo_reweight(const int64_t* __restrict__ r
 //            queue (at most qcap per step; the rest stay marked);
 //   relax    each group of G lanes fetches the adjacency [row_ptr[u],
 //            row_ptr[u+1]) of a queued vertex and relaxes it whole when it
-//            has up to 4G edges, two vertices at a time (up to 8 edge loads
-//            in flight per lane); a longer adjacency (a hub) is listed;
+//            has up to 8G edges, two vertices at a time (up to 8 edge loads
+//            in flight per lane, then strides of G); a longer adjacency (a
+//            hub) is listed;
 //   hubs     one wave per listed hub, the waves in parallel.
 // Dynamic LDS (32-bit words): dist[n4] tentative distances (kUnreached = not
 // reached), mark[nw4] the bitmap of vertices whose distance dropped since
@@ -395,8 +396,9 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
       }
 
       // -- relax: each group fetches its vertices' edge ranges itself --------
-      // A hub (more than 4G edges) goes to the hub list for a whole wave;
-      // when the list is full, its group relaxes the rest of it in strides.
+      // A hub (more than kBig edges) goes to the hub list for a whole wave;
+      // when the list is full, its group relaxes it like any other: four
+      // loads per lane, then the rest in strides of G.
       for (uint32_t i0 = grp; i0 < qn; i0 += 2 * kGroups) {
         int2 x[2][4];
         uint32_t du[2], rest_a[2], rest_b[2];
@@ -704,7 +706,7 @@ int run_johnson(const int64_t* row_ptr, const int32_t* col, const int32_t* w, in
     }
     const int grid = (int)std::min<int64_t>(n, (int64_t)cus * per_cu);
     mark(6);
-    // Lanes per adjacency: short adjacencies (<= 4G edges) go to groups of G
+    // Lanes per adjacency: short adjacencies (<= 8G edges) go to groups of G
     // lanes, longer ones to whole waves; G = 8 up to an average degree of 32,
     // then the smallest power of two with 4G >= the average degree.
     const int gsel = APSP_JO_G       ? APSP_JO_G
