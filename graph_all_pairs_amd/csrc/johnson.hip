@@ -73,6 +73,9 @@ constexpr int kHubUnroll = APSP_JO_HUB_UNROLL;  // edge loads in flight per lane
 #ifndef APSP_JO_HUB_MUL
 #define APSP_JO_HUB_MUL 8     // a hub has more than APSP_JO_HUB_MUL * G edges
 #endif
+#ifndef APSP_JO_ENTRIES
+#define APSP_JO_ENTRIES 2     // queued vertices a lane group relaxes at a time
+#endif
 #ifndef APSP_JO_G
 #define APSP_JO_G 0           // lanes per edge chunk; 0 = by average degree
 #endif
@@ -399,12 +402,13 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
       // A hub (more than kBig edges) goes to the hub list for a whole wave;
       // when the list is full, its group relaxes it like any other: four
       // loads per lane, then the rest in strides of G.
-      for (uint32_t i0 = grp; i0 < qn; i0 += 2 * kGroups) {
-        int2 x[2][4];
-        uint32_t du[2], rest_a[2], rest_b[2];
-        bool ok[2][4];
+      constexpr int kE = APSP_JO_ENTRIES;
+      for (uint32_t i0 = grp; i0 < qn; i0 += kE * kGroups) {
+        int2 x[kE][4];
+        uint32_t du[kE], rest_a[kE], rest_b[kE];
+        bool ok[kE][4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < kE; ++m) {
           const uint32_t i = i0 + m * kGroups;
           uint32_t a = 0, b = 0;
           rest_a[m] = rest_b[m] = 0;
@@ -437,12 +441,12 @@ jo_sssp(const int64_t* __restrict__ row_ptr, const int2* __restrict__ ew, int32_
           }
         }
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < kE; ++m)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (ok[m][j]) relax(du[m], x[m][j]);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < kE; ++m)
           for (uint32_t e = rest_a[m] + gl; e < rest_b[m]; e += G) relax(du[m], ew[e]);
       }
       __syncthreads();
