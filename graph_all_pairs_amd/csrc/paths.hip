@@ -19,7 +19,10 @@
 // registers, W's rows and D's rows stream through LDS in 16-deep chunks
 // (double buffered), u runs in increasing order and a candidate replaces the
 // pair only when strictly smaller, so the smallest u wins ties.  W[i][i] is
-// staged as inf (u != i).  Per candidate: add, compare, two selects.
+// staged as inf (u != i).  Per candidate: add, compare, two selects.  For
+// int32 inputs in a bounded range a second dense kernel packs value and index
+// into one key and runs at the min-plus product's instruction count (see
+// successors_packed); the range is checked on the device.
 //
 // Sparse weights.  Only u with w(i, u) < inf can win (any other candidate is
 // >= inf and never replaces the running value, which starts at inf), so for
@@ -73,12 +76,159 @@ __device__ __forceinline__ void ld4(const T* __restrict__ p, int64_t ld, int64_t
   }
 }
 
+// Device-side facts that choose the kernel: the number of finite
+// off-diagonal weights, and the range of the finite weights and distances.
+struct SuccStats {
+  unsigned long long edges;
+  int32_t wmin, wmax, dmin, dmax;
+};
+
+template <typename T>
+__device__ __forceinline__ void wave_minmax(int32_t& lo, int32_t& hi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+}
+
+// The statistics scans leave one partial per workgroup (no same-address
+// atomics: thousands of them serialise in L2) and one workgroup folds them.
+constexpr int kStatParts = 1024;
+
+// (c, lo, hi) summed / ranged over the workgroup; thread 0 holds the result.
+__device__ __forceinline__ void block_stats(unsigned long long& c, int32_t& lo, int32_t& hi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  wave_minmax<int32_t>(lo, hi);
+  __shared__ unsigned long long sc[16];
+  __shared__ int32_t slo[16], shi[16];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sc[wv] = c; slo[wv] = lo; shi[wv] = hi; }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int k = 1; k < (int)(blockDim.x >> 6); ++k) {
+      c += sc[k];
+      lo = min(lo, slo[k]);
+      hi = max(hi, shi[k]);
+    }
+}
+
+// Visits row r's entries (c, v) of an n x n matrix, 16-byte quads with four
+// in flight per thread when VEC (16-byte aligned rows), else one at a time.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void scan_row(const T* __restrict__ row, int64_t n, F&& visit) {
+  const int64_t full = VEC ? n / 4 : 0;  // quads wholly inside the row
+  int64_t q = threadIdx.x;
+  for (; q + 3 * blockDim.x < full; q += 4 * blockDim.x) {
+    T v[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load4(row + (q + k * blockDim.x) * 4, v[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) visit((q + k * blockDim.x) * 4 + e, v[k][e]);
+  }
+  for (; q < full; q += blockDim.x) {
+    T v[4];
+    load4(row + q * 4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) visit(q * 4 + e, v[e]);
+  }
+  for (int64_t c = full * 4 + threadIdx.x; c < n; c += blockDim.x) visit(c, row[c]);
+}
+
+// The finite off-diagonal weights w[i][u] < inf, u != i: their number and,
+// for int32, their range.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) succ_count(const T* __restrict__ W, int64_t ldw, int64_t n,
+                                                  T inf, SuccStats* __restrict__ part) {
+  uint32_t c = 0;
+  int32_t lo = INT32_MAX, hi = INT32_MIN;
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
+    scan_row<T, VEC>(W + i * ldw, n, [&](int64_t u, T v) {
+      const bool f = u != i && v < inf;
+      c += f;
+      if constexpr (std::is_same_v<T, int32_t>) {
+        lo = f ? min(lo, v) : lo;
+        hi = f ? max(hi, v) : hi;
+      }
+    });
+  unsigned long long cc = c;
+  block_stats(cc, lo, hi);
+  if (threadIdx.x == 0) {
+    part[blockIdx.x].edges = cc;
+    part[blockIdx.x].wmin = lo;
+    part[blockIdx.x].wmax = hi;
+  }
+}
+
+// The range of the finite distances (int32, dense graphs only).
+template <bool VEC>
+__global__ void __launch_bounds__(256) succ_dstats(const int32_t* __restrict__ D, int64_t ldd,
+                                                   int64_t n, int32_t inf,
+                                                   const SuccStats* __restrict__ st,
+                                                   SuccStats* __restrict__ part,
+                                                   unsigned long long max_sparse) {
+  if (st->edges <= max_sparse) return;  // the sparse kernel takes this matrix
+  int32_t lo = INT32_MAX, hi = INT32_MIN;
+  for (int64_t u = blockIdx.x; u < n; u += gridDim.x)
+    scan_row<int32_t, VEC>(D + u * ldd, n, [&](int64_t, int32_t v) {
+      const bool f = v < inf;
+      lo = f ? min(lo, v) : lo;
+      hi = f ? max(hi, v) : hi;
+    });
+  unsigned long long none = 0;
+  block_stats(none, lo, hi);
+  if (threadIdx.x == 0) {
+    part[blockIdx.x].dmin = lo;
+    part[blockIdx.x].dmax = hi;
+  }
+}
+
+// Folds the first `parts` partials into *st: the weight statistics (DIST
+// false), or the distance range of a dense matrix (DIST true).
+template <bool DIST>
+__global__ void __launch_bounds__(256) succ_fold(const SuccStats* __restrict__ part, int parts,
+                                                 SuccStats* __restrict__ st,
+                                                 unsigned long long max_sparse) {
+  if (DIST && st->edges <= max_sparse) return;
+  unsigned long long c = 0;
+  int32_t lo = INT32_MAX, hi = INT32_MIN;
+  for (int k = threadIdx.x; k < parts; k += blockDim.x) {
+    c += DIST ? 0 : part[k].edges;
+    lo = min(lo, DIST ? part[k].dmin : part[k].wmin);
+    hi = max(hi, DIST ? part[k].dmax : part[k].wmax);
+  }
+  block_stats(c, lo, hi);
+  if (threadIdx.x == 0) {
+    if (DIST) {
+      st->dmin = lo;
+      st->dmax = hi;
+    } else {
+      *st = SuccStats{c, lo, hi, INT32_MAX, INT32_MIN};
+    }
+  }
+}
+
+// Packed keys apply when every finite weight and distance is >= 0 and the
+// largest finite weight plus the largest finite distance is below both inf
+// and 2^(31 - shift): then (w + d) << shift | u < 2^31 for every finite
+// candidate, no finite candidate reaches inf, and 2^31 marks "no edge".
+__device__ __forceinline__ bool succ_packable(const SuccStats* st, int32_t inf, int shift) {
+  if (st->wmin < 0 || st->dmin < 0) return false;
+  const int64_t sum = (int64_t)max(st->wmax, 0) + (int64_t)max(st->dmax, 0);
+  return sum < (int64_t)inf && sum < (int64_t(1) << (31 - shift));
+}
+
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_t ldd,
            int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf, uint32_t tiles_per_row,
-           const unsigned long long* __restrict__ edges, unsigned long long max_sparse) {
-  if (*edges <= max_sparse) return;  // the sparse kernel takes this matrix
+           const SuccStats* __restrict__ st, unsigned long long max_sparse, int shift) {
+  if (st->edges <= max_sparse) return;  // the sparse kernel takes this matrix
+  if constexpr (std::is_same_v<T, int32_t>)
+    if (succ_packable(st, inf, shift)) return;  // the packed kernel takes it
   __shared__ __attribute__((aligned(16))) T lds[4 * kKC * kLd];
   T* sA = lds;                  // [2][kKC][kLd]: sA[t][row] = W[row0 + row][u0 + t]
   T* sB = lds + 2 * kKC * kLd;  // [2][kKC][kLd]: sB[t][col] = D[u0 + t][col0 + col]
@@ -183,20 +333,130 @@ successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_
     }
 }
 
-__global__ void __launch_bounds__(64) succ_zero(unsigned long long* __restrict__ edges) {
-  if (threadIdx.x == 0) *edges = 0;
-}
+// Dense successors with packed keys (int32, see succ_packable): the operand
+// staged for (i, u) is w(i, u) << shift, for (u, j) it is d(u, j) << shift | u,
+// "no edge" (and u = i) is 2^31, and a candidate is their unsigned sum,
+// saturated.  Its minimum over u is (the least w + d) << shift | (the
+// smallest u that reaches it) -- the same argmin and tie rule as the kernel
+// above -- at the instruction cost of the min-plus product: two saturating
+// adds and one three-input minimum per pair of candidates.
+constexpr uint32_t kNoEdge = 0x80000000u;
 
-// The number of finite off-diagonal weights, w[i][u] < inf with u != i.
-template <typename T>
-__global__ void __launch_bounds__(256) succ_count(const T* __restrict__ W, int64_t ldw, int64_t n,
-                                                  T inf, unsigned long long* __restrict__ edges) {
-  unsigned long long c = 0;
-  for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
-    for (int64_t u = threadIdx.x; u < n; u += blockDim.x) c += (u != i && W[i * ldw + u] < inf);
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+successors_packed(const int32_t* __restrict__ W, int64_t ldw, const int32_t* __restrict__ D,
+                  int64_t ldd, int32_t* __restrict__ nxt, int64_t ldn, int64_t n, int32_t inf,
+                  uint32_t tiles_per_row, const SuccStats* __restrict__ st,
+                  unsigned long long max_sparse, int shift) {
+  if (st->edges <= max_sparse || !succ_packable(st, inf, shift)) return;
+  // Keys are kept as their int32 bit patterns (the vector LDS helpers take
+  // int32) and read back as uint32.
+  __shared__ __attribute__((aligned(16))) int32_t lds[4 * kKC * kLd];
+  int32_t* sA = lds;                  // [2][kKC][kLd]: key of W[row0 + row][u0 + t]
+  int32_t* sB = lds + 2 * kKC * kLd;  // [2][kKC][kLd]: key of D[u0 + t][col0 + col]
+  const int tid = threadIdx.x;
+  const int tc = tid % kThr, tr = tid / kThr;
+  const int64_t row0 = (int64_t)(blockIdx.x / tiles_per_row) * kT;
+  const int64_t col0 = (int64_t)(blockIdx.x % tiles_per_row) * kT;
+
+  uint32_t acc[kR][kR];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-  if ((threadIdx.x & 63) == 0 && c) atomicAdd(edges, c);
+  for (int i = 0; i < kR; ++i)
+#pragma unroll
+    for (int j = 0; j < kR; ++j) acc[i][j] = 0xFFFFFFFFu;
+
+  int32_t ga[kLoads][4], gb[kLoads][4];
+  auto fetch = [&](int64_t u0) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int q = tid + l * kThreads;
+      const int r = q / (kKC / 4), uq = q % (kKC / 4);
+      ld4<int32_t, VEC>(W, ldw, n, n, row0 + r, u0 + uq * 4, inf, ga[l]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)  // u != i: the vertex itself is never its own first hop
+        if (row0 + r == u0 + uq * 4 + e) ga[l][e] = inf;
+      const int ur = q / (kT / 4), cq = q % (kT / 4);
+      ld4<int32_t, VEC>(D, ldd, n, n, u0 + ur, col0 + cq * 4, inf, gb[l]);
+    }
+  };
+  auto stash = [&](int buf, int64_t u0) {
+    int32_t* a = sA + buf * kKC * kLd;
+    int32_t* b = sB + buf * kKC * kLd;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int q = tid + l * kThreads;
+      const int r = q / (kKC / 4), uq = q % (kKC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[(uq * 4 + e) * kLd + r] =
+            (int32_t)(ga[l][e] < inf ? (uint32_t)ga[l][e] << shift : kNoEdge);
+      const int ur = q / (kT / 4), cq = q % (kT / 4);
+      const uint32_t u = (uint32_t)(u0 + ur);
+      int32_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (int32_t)(gb[l][e] < inf ? ((uint32_t)gb[l][e] << shift) | u : kNoEdge);
+      store4(b + ur * kLd + cq * 4, v);
+    }
+  };
+
+  const int64_t chunks = (n + kKC - 1) / kKC;
+  fetch(0);
+  stash(0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int64_t c = 0; c < chunks; ++c) {
+    const int buf = (int)(c & 1);
+    if (c + 1 < chunks) fetch((c + 1) * kKC);
+    const int32_t* a = sA + buf * kKC * kLd;
+    const int32_t* b = sB + buf * kKC * kLd;
+#pragma unroll 2
+    for (int t = 0; t < kKC; t += 2) {
+      uint32_t a0[kR], b0[kR], a1[kR], b1[kR];
+#pragma unroll
+      for (int gi = 0; gi < kR / 4; ++gi) {
+        int32_t v[4];
+        load4(a + t * kLd + gi * kGroupStride + tr * 4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a0[gi * 4 + i] = v[i];
+        load4(a + (t + 1) * kLd + gi * kGroupStride + tr * 4, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a1[gi * 4 + i] = v[i];
+        load4(b + t * kLd + gi * kGroupStride + tc * 4, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b0[gi * 4 + j] = v[j];
+        load4(b + (t + 1) * kLd + gi * kGroupStride + tc * 4, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b1[gi * 4 + j] = v[j];
+      }
+#pragma unroll
+      for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int j = 0; j < kR; ++j)
+          acc[i][j] = min(acc[i][j], min(__builtin_elementwise_add_sat(a0[i], b0[j]),
+                                         __builtin_elementwise_add_sat(a1[i], b1[j])));
+    }
+    if (c + 1 < chunks) stash(buf ^ 1, (c + 1) * kKC);
+    __syncthreads();
+  }
+
+  const uint32_t mask = (1u << shift) - 1u;
+#pragma unroll
+  for (int gi = 0; gi < kR / 4; ++gi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = row0 + gi * kGroupStride + tr * 4 + i;
+      if (r >= n) continue;
+#pragma unroll
+      for (int gj = 0; gj < kR / 4; ++gj)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = col0 + gj * kGroupStride + tc * 4 + j;
+          if (col >= n) continue;
+          const uint32_t k = acc[gi * 4 + i][gj * 4 + j];
+          nxt[r * ldn + col] = r == col ? (int32_t)r : (k < kNoEdge ? (int32_t)(k & mask) : -1);
+        }
+    }
 }
 
 constexpr int kSThreads = 256;
@@ -207,8 +467,8 @@ template <typename T, bool VEC>
 __global__ void __launch_bounds__(kSThreads)
 successors_sparse(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_t ldd,
                   int32_t* __restrict__ nxt, int64_t ldn, int64_t n, T inf,
-                  const unsigned long long* __restrict__ edges, unsigned long long max_sparse) {
-  if (*edges > max_sparse) return;  // the dense kernel takes this matrix
+                  const SuccStats* __restrict__ st, unsigned long long max_sparse) {
+  if (st->edges > max_sparse) return;  // a dense kernel takes this matrix
   __shared__ int32_t lu[kCap];
   __shared__ T lw[kCap];
   __shared__ int32_t wsum[kSThreads / 64];
@@ -330,29 +590,53 @@ int run_successors(const T* w, int64_t ldw, const T* d, int64_t ldd, int32_t* nx
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = al16(w) && al16(d) && ldw % 4 == 0 && ldd % 4 == 0;
-  unsigned long long* edges = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&edges), sizeof(unsigned long long), s) != hipSuccess) {
+  // stats[0]: the folded statistics; stats[1 .. parts]: per-workgroup partials.
+  const int parts = (int)std::min<int64_t>(n, kStatParts);
+  SuccStats* stats = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&stats), sizeof(SuccStats) * (1 + parts), s) !=
+      hipSuccess) {
     (void)apsp_detail_launch_status();
     return APSP_ERR_LAUNCH;
   }
   const unsigned long long max_sparse = (unsigned long long)n * (unsigned long long)n / 16;
-  hipLaunchKernelGGL(succ_zero, dim3(1), dim3(64), 0, s, edges);
-  hipLaunchKernelGGL(succ_count<T>, dim3((unsigned)std::min<int64_t>(n, 4096)), dim3(256), 0, s, w,
-                     ldw, n, inf, edges);
+  int shift = 0;  // bits that hold a vertex index: n <= 2^shift
+  while ((int64_t(1) << shift) < n) ++shift;
+  SuccStats* part = stats + 1;
+  const bool wvec = al16(w) && ldw % 4 == 0, dvec = al16(d) && ldd % 4 == 0;
+  if (wvec)
+    hipLaunchKernelGGL((succ_count<T, true>), dim3(parts), dim3(256), 0, s, w, ldw, n, inf, part);
+  else
+    hipLaunchKernelGGL((succ_count<T, false>), dim3(parts), dim3(256), 0, s, w, ldw, n, inf, part);
+  hipLaunchKernelGGL(succ_fold<false>, dim3(1), dim3(256), 0, s, part, parts, stats, max_sparse);
+  if constexpr (std::is_same_v<T, int32_t>) {
+    if (dvec)
+      hipLaunchKernelGGL(succ_dstats<true>, dim3(parts), dim3(256), 0, s, d, ldd, n, inf, stats,
+                         part, max_sparse);
+    else
+      hipLaunchKernelGGL(succ_dstats<false>, dim3(parts), dim3(256), 0, s, d, ldd, n, inf, stats,
+                         part, max_sparse);
+    hipLaunchKernelGGL(succ_fold<true>, dim3(1), dim3(256), 0, s, part, parts, stats, max_sparse);
+  }
   const dim3 grid((unsigned)(tpr * tpr));
   if (vec) {
     hipLaunchKernelGGL((successors<T, true>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt, ldn,
-                       n, inf, (uint32_t)tpr, edges, max_sparse);
+                       n, inf, (uint32_t)tpr, stats, max_sparse, shift);
+    if constexpr (std::is_same_v<T, int32_t>)
+      hipLaunchKernelGGL((successors_packed<true>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt,
+                         ldn, n, inf, (uint32_t)tpr, stats, max_sparse, shift);
     hipLaunchKernelGGL((successors_sparse<T, true>), dim3((unsigned)n), dim3(kSThreads), 0, s, w, ldw,
-                       d, ldd, nxt, ldn, n, inf, edges, max_sparse);
+                       d, ldd, nxt, ldn, n, inf, stats, max_sparse);
   } else {
     hipLaunchKernelGGL((successors<T, false>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd, nxt,
-                       ldn, n, inf, (uint32_t)tpr, edges, max_sparse);
+                       ldn, n, inf, (uint32_t)tpr, stats, max_sparse, shift);
+    if constexpr (std::is_same_v<T, int32_t>)
+      hipLaunchKernelGGL((successors_packed<false>), grid, dim3(kThreads), 0, s, w, ldw, d, ldd,
+                         nxt, ldn, n, inf, (uint32_t)tpr, stats, max_sparse, shift);
     hipLaunchKernelGGL((successors_sparse<T, false>), dim3((unsigned)n), dim3(kSThreads), 0, s, w,
-                       ldw, d, ldd, nxt, ldn, n, inf, edges, max_sparse);
+                       ldw, d, ldd, nxt, ldn, n, inf, stats, max_sparse);
   }
   const int st_launch = apsp_detail_launch_status();
-  (void)hipFreeAsync(edges, s);
+  (void)hipFreeAsync(stats, s);
   return st_launch;
 }
 

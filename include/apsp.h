@@ -244,9 +244,13 @@ int apsp_fw_host_plan(int64_t n, int64_t elem_bytes, int64_t device_bytes, int64
  * whose weights sum to d[i][j] when every weight on it is positive.
  * Work: n^3 candidates when w has more than n^2/16 finite off-diagonal
  * entries; else only the neighbours of each i are tried (n candidates per
- * edge).  The same matrix either way.  Asynchronous on `stream` (the choice
- * is made on the device); uses 8 bytes of stream-ordered scratch.  Errors as
- * for apsp_fw_i32.
+ * edge).  For n^3 candidates in int32, when every finite weight and distance
+ * is >= 0 and the largest finite weight plus the largest finite distance is
+ * below inf and 2^(31 - ceil(log2 n)), each candidate is one 32-bit key
+ * (w + d) << ceil(log2 n) | u and the argmin is a minimum of keys.  The same
+ * matrix in every case.  Asynchronous on `stream` (the choices are made on
+ * the device); uses 24 * (1 + min(n, 1024)) bytes of stream-ordered
+ * scratch.  Errors as for apsp_fw_i32.
  */
 int apsp_successors_i32(const int32_t *w, int64_t ldw, const int32_t *d, int64_t ldd,
                         int32_t *nxt, int64_t ldn, int64_t n, int32_t inf, void *stream);

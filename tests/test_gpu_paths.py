@@ -72,6 +72,28 @@ def test_int32_successors_dense_side(dev, orc, n):
     assert np.array_equal(gpu_successors(dev, w, d), orc.successors(w, d, INF))
 
 
+# Dense int32 matrices take packed keys ((w + d) << shift | u in 32 bits)
+# when every finite weight and distance is >= 0 and the largest finite
+# weight plus the largest finite distance is below inf and 2^(31 - shift),
+# shift = ceil(log2 n); otherwise the (value, index) kernel.  n = 300 gives
+# shift 9 and a bound of 2^22: near-tied weights around 2^20 stay below it,
+# around 2^21 they cross it.  Both sides match the oracle bit for bit.
+
+@pytest.mark.parametrize("base", [1 << 20, 1 << 21])
+def test_int32_successors_dense_around_the_packed_bound(dev, orc, base):
+    print(f"case successors i32 dense weights base={base}", flush=True)
+    n = 300
+    rng = np.random.default_rng(base % 1000 + 7)
+    w = (base + rng.integers(0, 4, size=(n, n))).astype(np.int32)
+    w[rng.random((n, n)) < 0.5] = INF
+    np.fill_diagonal(w, 0)
+    d = orc.fw_i32(w)
+    fin = d[d < INF]
+    packed = int(w[(w < INF)].max()) + int(fin.max()) < (1 << 22)
+    assert packed == (base == 1 << 20)
+    assert np.array_equal(gpu_successors(dev, w, d), orc.successors(w, d, INF))
+
+
 def test_int32_successors_hub_rows_take_several_gathers(dev, orc):
     # rows with more neighbours than one gather holds (2048), in a sparse matrix
     print("case successors i32 hub rows n=2500", flush=True)
