@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "apsp.h"
 #include "detail.h"
@@ -93,6 +94,108 @@ fw_batched(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stri
   }
 }
 
+// f(integral_constant<int, s>) for s = 0, 1, ..., in order.
+template <int... S, typename F>
+__device__ __forceinline__ void for_each_slot(std::integer_sequence<int, S...>, F&& f) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+
+// One wave closes one graph of NB = 8 R vertices (NB <= 88), with no
+// barrier between waves: lane (lr, lc) = (lane / 8, lane % 8) holds the
+// elements (8 ri + lr, 8 cj + lc), ri, cj < R.  Pivot pairs (t, t + 1) come in
+// increasing order and each element sees the same operations as in
+// close_block_t, so the results are bit-identical to that closure.  A
+// published pivot vector v is stored as p[8][16], v[8 q + r] at p[r][q], so a
+// lane reads its R values from one 16-aligned run.
+template <typename T, int NB, bool EDGE>
+__global__ void __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(2)))
+fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf) {
+  static_assert(NB % 8 == 0 && NB <= 88, "eight lanes per dimension; the tile fits two waves/SIMD");
+  constexpr int R = NB / 8;
+  // [buffer][column t, column t+1, row t, row t+1][8][16]
+  __shared__ __attribute__((aligned(16))) T lds[2][4][128];
+  const int lr = threadIdx.x >> 3, lc = threadIdx.x & 7;
+  for (int64_t g = blockIdx.x; g < batch; g += gridDim.x) {
+    T* m = d + g * stride;
+    T acc[R][R];
+#pragma unroll
+    for (int ri = 0; ri < R; ++ri) {
+      const int i = 8 * ri + lr;
+      const T* row = m + (int64_t)i * ld + lc;  // element (i, 8 cj + lc) at row[8 cj]
+#pragma unroll
+      for (int cj = 0; cj < R; ++cj)
+        acc[ri][cj] = (!EDGE || (i < n && 8 * cj + lc < n)) ? row[8 * cj] : inf;
+    }
+    // Pivots 8 s + owner and 8 s + owner + 1 into buffer buf.
+    auto publish = [&](int buf, int owner, auto slot) {
+      constexpr int s = decltype(slot)::value;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (lc == owner + h) {
+#pragma unroll
+          for (int ri = 0; ri < R; ++ri) lds[buf][h][lr * 16 + ri] = acc[ri][s];
+        }
+        if (lr == owner + h) {
+#pragma unroll
+          for (int cj = 0; cj < R; ++cj) lds[buf][2 + h][lc * 16 + cj] = acc[s][cj];
+        }
+      }
+    };
+    publish(0, 0, std::integral_constant<int, 0>{});
+    __syncthreads();
+    int buf = 0;
+    for_each_slot(std::make_integer_sequence<int, R>{}, [&](auto slot) {
+        constexpr int s = decltype(slot)::value;
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+          const int t1 = 8 * s + 2 * c + 1;
+          const T* base = &lds[buf][0][0];
+          T b0[R], b1[R];
+#pragma unroll
+          for (int k = 0; k < R; ++k) {
+            b0[k] = base[256 + lc * 16 + k];
+            b1[k] = base[384 + lc * 16 + k];
+          }
+          const int q1 = (t1 & 7) * 16 + (t1 >> 3);
+          const T d_t_t1 = base[256 + q1];  // D[t][t+1]
+          const T d_t1_t = base[q1];        // D[t+1][t]
+#pragma unroll
+          for (int k = 0; k < R; ++k) b1[k] = mp_min(b1[k], d_t1_t + b0[k]);
+          // The column values are read one row at a time: the tile and the row
+          // vectors already hold most of the registers.
+#pragma unroll
+          for (int ri = 0; ri < R; ++ri) {
+            const T a0 = base[lr * 16 + ri];
+            const T a1 = mp_min(base[128 + lr * 16 + ri], a0 + d_t_t1);
+#pragma unroll
+            for (int cj = 0; cj < R; ++cj)
+              acc[ri][cj] = mp_min3(acc[ri][cj], a0 + b0[cj], a1 + b1[cj]);
+          }
+          buf ^= 1;
+          if (c < 3) {
+            publish(buf, 2 * c + 2, std::integral_constant<int, s>{});
+          } else if constexpr (s + 1 < R) {
+            publish(buf, 0, std::integral_constant<int, s + 1>{});
+          }
+          __syncthreads();
+        }
+    });
+    // Recompute the addresses here rather than keep the loads' row pointers
+    // live through the closure.
+    int lr_s = lr, lc_s = lc;
+    asm volatile("" : "+v"(lr_s), "+v"(lc_s));
+#pragma unroll
+    for (int ri = 0; ri < R; ++ri) {
+      const int i = 8 * ri + lr_s;
+      T* row = m + (int64_t)i * ld + lc_s;
+#pragma unroll
+      for (int cj = 0; cj < R; ++cj)
+        if (!EDGE || (i < n && 8 * cj + lc_s < n)) row[8 * cj] = acc[ri][cj];
+    }
+  }
+}
+
 template <typename T>
 bool inf_ok(T inf);
 template <>
@@ -111,6 +214,29 @@ void launch(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf, b
   } else {
     if (vec) hipLaunchKernelGGL((fw_batched<T, NB, RT, true, true>), grid, block, 0, s, d, batch, n, ld, stride, inf);
     else hipLaunchKernelGGL((fw_batched<T, NB, RT, false, true>), grid, block, 0, s, d, batch, n, ld, stride, inf);
+  }
+}
+
+// The one-wave kernel where it measured faster than the workgroup closure
+// (8192 complete graphs): NB = 72 by 1.3-1.4x in both types, NB = 80 by 1.1x
+// in int32.  At NB = 88 the two tie; at NB = 96 and 104 the tile needs one
+// wave per SIMD and runs 0.7-0.9x.
+template <typename T, int NB>
+constexpr bool kWaveClass = NB == 72 || (NB == 80 && std::is_same_v<T, int32_t>);
+
+template <typename T, int NB>
+void launch_class(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf, bool vec,
+                  hipStream_t s) {
+  if constexpr (!kWaveClass<T, NB>) {
+    launch<T, NB, 8>(d, batch, n, ld, stride, inf, vec, s);
+  } else {
+    const dim3 grid((unsigned)(batch < kMaxGrid ? batch : kMaxGrid));
+    if (n == NB)
+      hipLaunchKernelGGL((fw_batched_wave<T, NB, false>), grid, dim3(64), 0, s, d, batch, n, ld,
+                         stride, inf);
+    else
+      hipLaunchKernelGGL((fw_batched_wave<T, NB, true>), grid, dim3(64), 0, s, d, batch, n, ld,
+                         stride, inf);
   }
 }
 
@@ -141,8 +267,8 @@ int run_batched(T* d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T in
     case 6: launch<T, 48, 8>(d, batch, n, ld, stride, inf, vec, s); break;
     case 7: launch<T, 56, 8>(d, batch, n, ld, stride, inf, vec, s); break;
     case 8: launch<T, 64, 8>(d, batch, n, ld, stride, inf, vec, s); break;
-    case 9: launch<T, 72, 8>(d, batch, n, ld, stride, inf, vec, s); break;
-    case 10: launch<T, 80, 8>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 9: launch_class<T, 72>(d, batch, n, ld, stride, inf, vec, s); break;
+    case 10: launch_class<T, 80>(d, batch, n, ld, stride, inf, vec, s); break;
     case 11: launch<T, 88, 8>(d, batch, n, ld, stride, inf, vec, s); break;
     case 12: launch<T, 96, 8>(d, batch, n, ld, stride, inf, vec, s); break;
     case 13: launch<T, 104, 8>(d, batch, n, ld, stride, inf, vec, s); break;

@@ -82,7 +82,7 @@ def test_batched_i32_er_exact(dev, n):
     assert np.array_equal(got, oracle.default().fw_batched_i32(w))
 
 
-@pytest.mark.parametrize("n", [4, 32, 48, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("n", [4, 32, 48, 64, 65, 72, 80, 96, 112, 128])
 def test_batched_i32_complete_padded_layout(dev, n):
     # ld > n and a gap between graphs; the smallest legal stride too
     print(f"batched i32 complete n={n}", flush=True)
@@ -92,7 +92,7 @@ def test_batched_i32_complete_padded_layout(dev, n):
     assert np.array_equal(run_batched(dev, w, INF, ld=n + 3), want)   # stride = (n-1)*ld + n
 
 
-@pytest.mark.parametrize("n", [8, 48, 64, 90, 128])
+@pytest.mark.parametrize("n", [8, 48, 64, 70, 77, 90, 128])
 def test_batched_i32_unaligned_scalar_path(dev, n):
     print(f"batched i32 unaligned n={n}", flush=True)
     w = gg.erdos_renyi_batch(11, n, 0.3, 1, 50, 300 + n)
@@ -112,7 +112,7 @@ def test_batched_i32_rings_closed_form(dev):
         assert all(np.array_equal(got[g], want) for g in range(9))
 
 
-@pytest.mark.parametrize("n", [5, 32, 40, 64, 72, 100, 128])
+@pytest.mark.parametrize("n", [5, 32, 40, 64, 67, 72, 100, 128])
 def test_batched_f32_matches_oracle_and_single_entry(dev, n):
     print(f"batched f32 n={n}", flush=True)
     w = gg.complete_f32_batch(13, n, 400 + n)
@@ -150,6 +150,24 @@ def test_batched_many_graphs_grid_stride(dev):
     ga.fw_batched(t)
     torch.cuda.synchronize()
     assert np.array_equal(t.cpu().numpy(), oracle.default().fw_batched_i32(w))
+
+
+@pytest.mark.parametrize("n", [65, 73])
+def test_batched_many_graphs_grid_stride_one_wave_classes(dev, n):
+    # 2^20 + 77 graphs of the one-wave size classes: 64 distinct graphs
+    # repeated on the device, every graph compared with the oracle's
+    print(f"batched many graphs n={n}", flush=True)
+    batch, distinct = (1 << 20) + 77, 64
+    w = gg.erdos_renyi_batch(distinct, n, 0.3, 1, 50, 600 + n)
+    want = torch.from_numpy(oracle.default().fw_batched_i32(w)).to(dev)
+    t = torch.from_numpy(w).to(dev).repeat(batch // distinct + 1, 1, 1)[:batch].contiguous()
+    ga.fw_batched(t)
+    torch.cuda.synchronize()
+    idx = torch.arange(batch, device=dev) % distinct
+    for c0 in range(0, batch, 1 << 16):
+        c1 = min(batch, c0 + (1 << 16))
+        assert torch.equal(t[c0:c1], want[idx[c0:c1]]), f"graphs {c0}..{c1}"
+    del t
 
 
 def test_batched_empty_and_wrapper_errors(dev):
