@@ -9,9 +9,13 @@
 // rate needs more than one wave per SIMD, and an odd wave count leaves part
 // of it unused, so this is the most the tile kernel's instruction stream can
 // reach on this device and clock.  It is reported next to the peak derived
-// from unit counts and clock.
+// from unit counts and clock.  A third mix replicates the successor
+// product's packed keys: two unsigned saturating adds and one unsigned
+// three-input min per pair of candidates.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "apsp.h"
 
@@ -26,6 +30,19 @@ __device__ __forceinline__ float ceil_min3(float a, float b, float c) {
   float r;
   asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+__device__ __forceinline__ uint32_t ceil_min3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_min3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// A candidate sum: wrapping for int32 and binary32, saturating for the
+// unsigned packed (sum, index) keys of the successor product.
+template <typename T>
+__device__ __forceinline__ T ceil_add(T a, T b) {
+  if constexpr (std::is_same_v<T, uint32_t>) return __builtin_elementwise_add_sat(a, b);
+  else return a + b;
 }
 
 template <typename T>
@@ -48,7 +65,7 @@ minplus_core(T* __restrict__ out, int iters) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = ceil_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+      for (int j = 0; j < 8; ++j) acc[i][j] = ceil_min3(acc[i][j], ceil_add(a0[i], b0[j]), ceil_add(a1[i], b1[j]));
   }
   T s = 0;
 #pragma unroll
@@ -106,6 +123,7 @@ int measure_best(double* relax_per_s) {
 }  // namespace
 
 extern "C" int apsp_minplus_ceiling(int arith, double* relax_per_s) {
-  if (relax_per_s == nullptr || (arith != 0 && arith != 1)) return APSP_ERR_INVALID_VALUE;
+  if (relax_per_s == nullptr || arith < 0 || arith > 2) return APSP_ERR_INVALID_VALUE;
+  if (arith == 2) return measure_best<uint32_t>(relax_per_s);
   return arith == 1 ? measure_best<float>(relax_per_s) : measure_best<int32_t>(relax_per_s);
 }

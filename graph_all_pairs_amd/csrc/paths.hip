@@ -343,7 +343,7 @@ successors(const T* __restrict__ W, int64_t ldw, const T* __restrict__ D, int64_
 constexpr uint32_t kNoEdge = 0x80000000u;
 
 template <bool VEC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 successors_packed(const int32_t* __restrict__ W, int64_t ldw, const int32_t* __restrict__ D,
                   int64_t ldd, int32_t* __restrict__ nxt, int64_t ldn, int64_t n, int32_t inf,
                   uint32_t tiles_per_row, const SuccStats* __restrict__ st,
@@ -410,7 +410,7 @@ successors_packed(const int32_t* __restrict__ W, int64_t ldw, const int32_t* __r
     if (c + 1 < chunks) fetch((c + 1) * kKC);
     const int32_t* a = sA + buf * kKC * kLd;
     const int32_t* b = sB + buf * kKC * kLd;
-#pragma unroll 2
+#pragma unroll 1
     for (int t = 0; t < kKC; t += 2) {
       uint32_t a0[kR], b0[kR], a1[kR], b1[kR];
 #pragma unroll

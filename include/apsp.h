@@ -411,7 +411,10 @@ int apsp_get_int32_arith(void);
  * device, in relaxations per second.  Runs a register-only replica of the
  * Phase-3 inner step (8 x 8 accumulators per thread, two candidates per
  * three-input min, no memory traffic) at 2 and at 4 waves per SIMD on the
- * null stream, synchronises, and reports the faster rate.  arith: 0 = int32 arithmetic, 1 = binary32.  Allocates
+ * null stream, synchronises, and reports the faster rate.  arith: 0 = int32
+ * arithmetic, 1 = binary32, 2 = the packed (sum, index) keys of
+ * apsp_successors_i32 (unsigned saturating adds, unsigned three-input min;
+ * candidates per second).  Allocates
  * and frees a small device buffer.  Returns APSP_ERR_INVALID_VALUE for a bad
  * argument, APSP_ERR_LAUNCH on a HIP failure.
  */
