@@ -58,10 +58,12 @@ DEFAULT_WORKLOAD = "complete-8192-i32"
 #  - binary32 adds/mins issue at 128 lanes per clock per CU (the rate behind
 #    the published 157.3 TFLOP/s fp32 vector figure, FMA = 2 flops):
 #    7.86e13 lane-instructions/s -> 5.24e13 relaxations/s;
-#  - int32 adds/mins issue at 64 lanes per clock per CU:
-#    3.93e13 lane-instructions/s -> 2.62e13 relaxations/s.
+#  - int32: the VOP2 add issues at 64 lanes per clock per CU, but the
+#    kernels write it in its VOP3 encoding, which co-issues: the
+#    register-only int32 mix with it measures above 2.62e13 relaxations/s
+#    (3.5e13).  So the int32 roof is the same dual-issue rate, 5.24e13.
 INSTR_PER_RELAX = 1.5
-VALU_LANE_OPS = {"f32": 256 * 128 * 2.4e9, "int32": 256 * 64 * 2.4e9}
+VALU_LANE_OPS = {"f32": 256 * 128 * 2.4e9, "int32": 256 * 128 * 2.4e9}
 PEAK_RELAX = {k: v / INSTR_PER_RELAX for k, v in VALU_LANE_OPS.items()}
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
@@ -764,7 +766,7 @@ def bench_paths(args) -> int:
                         "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "Tcandidates/s",
                         "frac": achieved / peak, "traffic": None, "avg_launch_ms": succ_ms,
                         "launches": args.steps,
-                        "note": "peak: int32 VALU rate / 4 instructions per candidate "
+                        "note": "peak: dual-issue VALU rate / 4 instructions per candidate "
                                 "(add, compare, two selects)"}
     log(f"timed {args.steps} steps: {ms_per_step:.1f} ms/step, successor pass {succ_ms:.2f} ms "
         f"({'neighbour lists' if sparse else 'dense product'}, {edges} edges)")

@@ -161,16 +161,16 @@ fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t
           const T d_t_t1 = base[256 + q1];  // D[t][t+1]
           const T d_t1_t = base[q1];        // D[t+1][t]
 #pragma unroll
-          for (int k = 0; k < R; ++k) b1[k] = mp_min(b1[k], d_t1_t + b0[k]);
+          for (int k = 0; k < R; ++k) b1[k] = mp_min(b1[k], mp_add(d_t1_t, b0[k]));
           // The column values are read one row at a time: the tile and the row
           // vectors already hold most of the registers.
 #pragma unroll
           for (int ri = 0; ri < R; ++ri) {
             const T a0 = base[lr * 16 + ri];
-            const T a1 = mp_min(base[128 + lr * 16 + ri], a0 + d_t_t1);
+            const T a1 = mp_min(base[128 + lr * 16 + ri], mp_add(a0, d_t_t1));
 #pragma unroll
             for (int cj = 0; cj < R; ++cj)
-              acc[ri][cj] = mp_min3(acc[ri][cj], a0 + b0[cj], a1 + b1[cj]);
+              acc[ri][cj] = mp_min3(acc[ri][cj], mp_add(a0, b0[cj]), mp_add(a1, b1[cj]));
           }
           buf ^= 1;
           if (c < 3) {

@@ -37,12 +37,19 @@ __device__ __forceinline__ uint32_t ceil_min3(uint32_t a, uint32_t b, uint32_t c
   return r;
 }
 
-// A candidate sum: wrapping for int32 and binary32, saturating for the
+// A candidate sum: wrapping for int32 (VOP3 form) and binary32, saturating for the
 // unsigned packed (sum, index) keys of the successor product.
 template <typename T>
 __device__ __forceinline__ T ceil_add(T a, T b) {
-  if constexpr (std::is_same_v<T, uint32_t>) return __builtin_elementwise_add_sat(a, b);
-  else return a + b;
+  if constexpr (std::is_same_v<T, uint32_t>) {
+    return __builtin_elementwise_add_sat(a, b);
+  } else if constexpr (std::is_same_v<T, int32_t>) {
+    T r;  // the tile kernels' form: the wrapping add in its VOP3 encoding
+    asm("v_add_u32_e64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  } else {
+    return a + b;
+  }
 }
 
 template <typename T>

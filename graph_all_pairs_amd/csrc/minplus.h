@@ -22,6 +22,17 @@ __device__ __forceinline__ float mp_min(float a, float b) {
   return r;
 }
 
+// A candidate sum.  int32: the wrapping add written in its VOP3 encoding.
+// With it the add, add, min3 mix issues about 1.4x faster on gfx950 than
+// with the VOP2 form the compiler picks for a + b (a register-only replica
+// measures 35 against 25-26 T relaxations/s); the result is the same add.
+__device__ __forceinline__ int32_t mp_add(int32_t a, int32_t b) {
+  int32_t r;
+  asm("v_add_u32_e64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float mp_add(float a, float b) { return a + b; }
+
 // min(a, b, c) as one v_min3.  Written as an instruction so that the compiler
 // keeps one three-input min per pair of candidates instead of re-balancing
 // the chain into two-input mins.
@@ -215,13 +226,13 @@ __device__ __forceinline__ void close_block_t(T (&acc)[RT][RT], T* __restrict__ 
         const T d_t_t1 = base[2 * NB + t + 1];  // D[t][t+1]
         const T d_t1_t = base[t + 1];           // D[t+1][t]
 #pragma unroll
-        for (int i = 0; i < RT; ++i) a1[i] = mp_min(a1[i], a0[i] + d_t_t1);
+        for (int i = 0; i < RT; ++i) a1[i] = mp_min(a1[i], mp_add(a0[i], d_t_t1));
 #pragma unroll
-        for (int j = 0; j < RT; ++j) b1[j] = mp_min(b1[j], d_t1_t + b0[j]);
+        for (int j = 0; j < RT; ++j) b1[j] = mp_min(b1[j], mp_add(d_t1_t, b0[j]));
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
-          for (int j = 0; j < RT; ++j) acc[i][j] = mp_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+          for (int j = 0; j < RT; ++j) acc[i][j] = mp_min3(acc[i][j], mp_add(a0[i], b0[j]), mp_add(a1[i], b1[j]));
 
         // publish the next pair into the other buffer
         if (cc == 0) {
