@@ -6,6 +6,8 @@ import this module.  The product path (``graph_all_pairs_amd``) never does.
 Functions mirror the C library:
   * ``fw_i32(m, k_end=None)`` / ``fw_f64(m, k_end=None)``: plain Floyd-Warshall
     on a copy of the matrix (pivots 0 .. k_end-1), returned as a new array;
+  * ``fw_in_steps(m, step, progress)``: the same recurrence run as
+    consecutive pivot ranges, reporting after each (long full-size runs);
   * ``sssp_rows_i32(w, inf, srcs)`` / ``sssp_rows_f64(w, inf, srcs)``:
     Dijkstra from each listed source, one output row per source;
   * ``fw_guarded(m, inf)``: Floyd-Warshall with negative weights allowed
@@ -56,6 +58,10 @@ def load(path: str = LIB):
     lib.oracle_fw_i32.restype = None
     lib.oracle_fw_f64.argtypes = [p, i64, i64, i64]
     lib.oracle_fw_f64.restype = None
+    lib.oracle_fw_range_i32.argtypes = [p, i64, i64, i64, i64]
+    lib.oracle_fw_range_i32.restype = None
+    lib.oracle_fw_range_f64.argtypes = [p, i64, i64, i64, i64]
+    lib.oracle_fw_range_f64.restype = None
     lib.oracle_fw_batched_i32.argtypes = [p, i64, i64, i64, i64]
     lib.oracle_fw_batched_i32.restype = None
     lib.oracle_fw_batched_f64.argtypes = [p, i64, i64, i64, i64]
@@ -113,6 +119,24 @@ class Oracle:
         n = a.shape[0]
         ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
         self.lib.oracle_fw_f64(a.ctypes.data, n, ld, n if k_end is None else int(k_end))
+        return a
+
+    def fw_in_steps(self, m: np.ndarray, step: int, progress=None) -> np.ndarray:
+        """The whole recurrence (int32 stays int32; floats in binary64) on a
+        copy, run as consecutive pivot ranges of `step` pivots.  After each
+        range, progress(k_done, n) is called; the result is the same as one
+        fw_i32 / fw_f64 call, since the ranges take the pivots in order."""
+        is_int = np.asarray(m).dtype == np.int32
+        a = np.array(m, dtype=np.int32 if is_int else np.float64, order="C", copy=True)
+        n = a.shape[0]
+        ld = a.shape[1] if a.ndim == 2 and n else max(n, 1)
+        fn = self.lib.oracle_fw_range_i32 if is_int else self.lib.oracle_fw_range_f64
+        step = max(1, int(step))
+        for k0 in range(0, n, step):
+            k1 = min(n, k0 + step)
+            fn(a.ctypes.data, n, ld, k0, k1)
+            if progress is not None:
+                progress(k1, n)
         return a
 
     def fw_batched_i32(self, m: np.ndarray) -> np.ndarray:

@@ -67,11 +67,15 @@ int oracle_max_threads(void) {
 
 int oracle_version(void) { return 2; }
 
-/* Floyd-Warshall on int32 distances, in place; pivots k = 0 .. k_end-1. */
-void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {
+/* Floyd-Warshall on int32 distances, in place; pivots k = k_begin .. k_end-1
+ * taken in order.  Given the recurrence's state after pivots 0 .. k_begin-1,
+ * it leaves the state after pivots 0 .. k_end-1, so a long run can be split
+ * into consecutive ranges. */
+void oracle_fw_range_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_begin, int64_t k_end) {
+  if (k_begin < 0) k_begin = 0;
   if (k_end > n) k_end = n;
   int nt = oracle_max_threads();
-  for (int64_t k = 0; k < k_end; ++k) {
+  for (int64_t k = k_begin; k < k_end; ++k) {
     const int32_t *row_k = d + k * ld;
 #pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t i = 0; i < n; ++i) {
@@ -85,11 +89,18 @@ void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {
   }
 }
 
-/* Floyd-Warshall on binary64 distances, in place; pivots k = 0 .. k_end-1. */
-void oracle_fw_f64(double *d, int64_t n, int64_t ld, int64_t k_end) {
+/* Pivots 0 .. k_end-1 (the whole recurrence when k_end >= n). */
+void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {
+  oracle_fw_range_i32(d, n, ld, 0, k_end);
+}
+
+/* Floyd-Warshall on binary64 distances, in place; pivots k = k_begin ..
+ * k_end-1 in order, as for int32 above. */
+void oracle_fw_range_f64(double *d, int64_t n, int64_t ld, int64_t k_begin, int64_t k_end) {
+  if (k_begin < 0) k_begin = 0;
   if (k_end > n) k_end = n;
   int nt = oracle_max_threads();
-  for (int64_t k = 0; k < k_end; ++k) {
+  for (int64_t k = k_begin; k < k_end; ++k) {
     const double *row_k = d + k * ld;
 #pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t i = 0; i < n; ++i) {
@@ -101,6 +112,10 @@ void oracle_fw_f64(double *d, int64_t n, int64_t ld, int64_t k_end) {
       }
     }
   }
+}
+
+void oracle_fw_f64(double *d, int64_t n, int64_t ld, int64_t k_end) {
+  oracle_fw_range_f64(d, n, ld, 0, k_end);
 }
 
 /*

@@ -27,16 +27,19 @@ MUTANTS = {
                            "int64_t cand = d_ik + (int64_t)row_i[j];"),
     "fw_max_not_min": ("if (cand < row_i[j]) row_i[j] = (int32_t)cand;",
                        "if (cand > row_i[j]) row_i[j] = (int32_t)cand;"),
-    "fw_skips_first_pivot": ("for (int64_t k = 0; k < k_end; ++k) {\n    const int32_t",
-                             "for (int64_t k = 1; k < k_end; ++k) {\n    const int32_t"),
-    "fw_skips_last_pivot": ("void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {\n  if (k_end > n) k_end = n;",
-                            "void oracle_fw_i32(int32_t *d, int64_t n, int64_t ld, int64_t k_end) {\n  if (k_end > n - 1) k_end = n - 1;"),
+    "fw_skips_first_pivot": ("for (int64_t k = k_begin; k < k_end; ++k) {\n    const int32_t",
+                             "for (int64_t k = k_begin + 1; k < k_end; ++k) {\n    const int32_t"),
+    "fw_skips_last_pivot": ("int64_t k_begin, int64_t k_end) {\n  if (k_begin < 0) k_begin = 0;\n  if (k_end > n) k_end = n;\n  int nt = oracle_max_threads();\n  for (int64_t k = k_begin; k < k_end; ++k) {\n    const int32_t",
+                            "int64_t k_begin, int64_t k_end) {\n  if (k_begin < 0) k_begin = 0;\n  if (k_end > n - 1) k_end = n - 1;\n  int nt = oracle_max_threads();\n  for (int64_t k = k_begin; k < k_end; ++k) {\n    const int32_t"),
     "fw_diagonal_only_rows": ("for (int64_t i = 0; i < n; ++i) {\n      int32_t *row_i",
                               "for (int64_t i = 0; i < n; i += 2) {\n      int32_t *row_i"),
     # Floyd-Warshall, binary64
     "fw64_max_not_min": ("if (cand < row_i[j]) row_i[j] = cand;",
                          "if (cand > row_i[j]) row_i[j] = cand;"),
     "fw64_transposed_dik": ("double d_ik = row_i[k];", "double d_ik = d[k * ld + i];"),
+    "fw64_skips_first_pivot": ("for (int64_t k = k_begin; k < k_end; ++k) {\n    const double",
+                               "for (int64_t k = k_begin + 1; k < k_end; ++k) {\n    const double"),
+    "fw64_wrong_index_dkj": ("double cand = d_ik + row_k[j];", "double cand = d_ik + row_k[i];"),
     # Dijkstra, int32
     "sssp_extracts_max": ("(u < 0 || dist[v] < dist[u])) u = v;\n    if (u < 0) break;\n    settled[u] = 1;\n    const int32_t",
                           "(u < 0 || dist[v] > dist[u])) u = v;\n    if (u < 0) break;\n    settled[u] = 1;\n    const int32_t"),

@@ -570,3 +570,31 @@ def test_successors_on_a_grid_closed_form(orc):
             else:
                 want = a + C
             assert nxt[a, b] == want, (a, b)
+
+
+def test_fw_in_steps_takes_the_pivots_in_order(orc):
+    """Consecutive pivot ranges are the recurrence itself: the hand-worked
+    example's states after each pivot, and the one-call result on random
+    graphs, for every range length."""
+    g = read_golden("hand4_fw.txt", INF)
+    w4 = g["input"].astype(np.int32)
+    seen = []
+    got = orc.fw_in_steps(w4, 1, lambda k, n: seen.append(k))
+    assert seen == [1, 2, 3, 4]
+    assert np.array_equal(got, g["final"])
+    for k_end, key in [(1, "after_k 1"), (2, "after_k 2"), (3, "after_k 3")]:
+        part = orc.fw_i32(w4, k_end=k_end)
+        assert np.array_equal(part, g[key])
+    rng = np.random.default_rng(5)
+    for step in (1, 2, 3, 7, 50):
+        w = random_small_graph(rng, 7, 0.4, 30, INF)
+        assert np.array_equal(orc.fw_in_steps(w, step).astype(np.int64),
+                              brute_force_apsp(w, INF).astype(np.int64))
+        w = random_small_graph(rng, 61, 0.1, 30, INF)
+        assert np.array_equal(orc.fw_in_steps(w, step), orc.fw_i32(w))
+        wf = random_small_graph(rng, 7, 0.5, 4, np.inf, floats=True)
+        want = brute_force_apsp(wf, np.inf).astype(np.float64)
+        gotf = orc.fw_in_steps(wf, step)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isinf(gotf), ~fin)
+        assert np.allclose(gotf[fin], want[fin], rtol=1e-12)
