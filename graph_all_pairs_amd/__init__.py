@@ -62,6 +62,7 @@ EXPORTS = (
     "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
     "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_fw_host_plan", "apsp_successors_i32",
     "apsp_successors_f32", "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
+    "apsp_fw_i32_noalloc",
 )
 
 _lib = None
@@ -111,6 +112,7 @@ def load(path: str | None = None):
     sig = {
         "apsp_fw_i32": ([vp, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_f32": ([vp, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_fw_i32_noalloc": ([vp, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_rounds_i32": ([vp, i64, i64, i32, i64, i64, vp], ctypes.c_int),
         "apsp_fw_rounds_f32": ([vp, i64, i64, f32, i64, i64, vp], ctypes.c_int),
         "apsp_fw_timed_i32": ([vp, i64, i64, i32, vp, dp, lp, ip], ctypes.c_int),
@@ -155,6 +157,10 @@ def load(path: str | None = None):
 
 def apsp_fw_i32(d_ptr: int, n: int, ld: int, inf: int, stream: int = 0) -> int:
     return load().apsp_fw_i32(d_ptr or None, n, ld, inf, stream or None)
+
+
+def apsp_fw_i32_noalloc(d_ptr: int, n: int, ld: int, inf: int, stream: int = 0) -> int:
+    return load().apsp_fw_i32_noalloc(d_ptr or None, n, ld, inf, stream or None)
 
 
 def apsp_fw_f32(d_ptr: int, n: int, ld: int, inf: float, stream: int = 0) -> int:

@@ -833,6 +833,15 @@ __global__ void __launch_bounds__(kThreads) diag_negative(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Scratch for apsp_fw_i32_noalloc: the scan result of an int32 call (two
+// words) in a file-scope device array, so that entry point allocates
+// nothing.  Every call of it on one GPU shares that GPU's copy; each call
+// clears the two words (scan_zero) before its scan writes them.
+// ---------------------------------------------------------------------------
+constexpr int kNoAllocScratchWords = 64;  // 256 bytes; an int32 call needs 2
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchWords];
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 thread_local int g_last_hip_error = 0;
@@ -871,6 +880,34 @@ int device_cus() {
     if (c > 0) return c;
   }
   return 256;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy of the array at its own address).  In
+// host code the array's name is only a host-side stand-in; this address is
+// what kernels and copies take.
+std::atomic<int32_t*> g_noalloc_scratch[kMaxDevices];
+
+int noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int)hipGetLastError();
+    return APSP_ERR_NO_DEVICE;
+  }
+  int32_t* p = g_noalloc_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || addr == nullptr) {
+      g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      (void)hipGetLastError();
+      return APSP_ERR_LAUNCH;
+    }
+    p = static_cast<int32_t*>(addr);
+    g_noalloc_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return APSP_OK;
 }
 
 template <typename T>
@@ -940,11 +977,11 @@ int launch_status() {
   return APSP_OK;
 }
 
-// Rounds [r0, r1).  For int32 matrices `scratch` (may be null) holds the
+// Rounds [r0, r1).  For int32 matrices `scan_buf` (may be null) holds the
 // scan result that selects binary32 or int32 arithmetic inside the kernels.
 template <typename T, bool VEC>
 void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
-                    const int32_t* scratch, PhaseTimer* tm) {
+                    const int32_t* scan_buf, PhaseTimer* tm) {
   const int64_t nb = (n + kB - 1) / kB;
   auto mark = [&](int k, bool before) {
     if (tm) tm->mark(k, before);
@@ -954,7 +991,7 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   mark(kKindPhase1, true);
   if constexpr (std::is_same_v<T, int32_t>)
     hipLaunchKernelGGL((fw_phase1_i32<VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0,
-                       scratch);
+                       scan_buf);
   else
     hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
   mark(kKindPhase1, false);
@@ -963,7 +1000,7 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     mark(kKindPhase2, true);
     if constexpr (std::is_same_v<T, int32_t>)
       hipLaunchKernelGGL((fw_phase2_i32<VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n,
-                         ld, inf, K, nb, scratch);
+                         ld, inf, K, nb, scan_buf);
     else
       hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n, ld,
                          inf, K, nb);
@@ -973,7 +1010,7 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     mark(kKindPhase3, true);
     if constexpr (std::is_same_v<T, int32_t>)
       hipLaunchKernelGGL((fw_phase3_i32<VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n,
-                         ld, inf, K, nb, fuse, scratch);
+                         ld, inf, K, nb, fuse, scan_buf);
     else
       hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
                          inf, K, nb, fuse);
@@ -984,22 +1021,22 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
 // Scan + conversion around the rounds of an int32 call.
 template <bool VEC>
 void enqueue_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t r0, int64_t r1,
-                 hipStream_t s, int32_t* scratch, PhaseTimer* tm) {
+                 hipStream_t s, int32_t* scan_buf, PhaseTimer* tm) {
   const int64_t rows = n < kScanBlocks ? n : kScanBlocks;
-  if (scratch) {
+  if (scan_buf) {
     if (tm) tm->mark(kKindConvert, true);
-    hipLaunchKernelGGL(scan_zero, dim3(1), dim3(64), 0, s, scratch);
+    hipLaunchKernelGGL(scan_zero, dim3(1), dim3(64), 0, s, scan_buf);
     hipLaunchKernelGGL((scan_i32<VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n, ld, inf,
-                       scratch);
+                       scan_buf);
     hipLaunchKernelGGL((convert_i32<VEC, true>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n,
-                       ld, inf, scratch);
+                       ld, inf, scan_buf);
     if (tm) tm->mark(kKindConvert, false);
   }
-  enqueue_rounds<int32_t, VEC>(d, n, ld, inf, r0, r1, s, scratch, tm);
-  if (scratch) {
+  enqueue_rounds<int32_t, VEC>(d, n, ld, inf, r0, r1, s, scan_buf, tm);
+  if (scan_buf) {
     if (tm) tm->mark(kKindConvert, true);
     hipLaunchKernelGGL((convert_i32<VEC, false>), dim3((unsigned)rows), dim3(kThreads), 0, s, d,
-                       n, ld, inf, scratch);
+                       n, ld, inf, scan_buf);
     if (tm) tm->mark(kKindConvert, false);
   }
 }
@@ -1009,7 +1046,7 @@ void enqueue_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t r0, int
 // synchronised) before the stream-ordered scratch is released.
 template <typename T>
 int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream,
-        PhaseTimer* tm, int32_t* scan_out) {
+        PhaseTimer* tm, int32_t* scan_out, int32_t* fixed_scan_buf = nullptr) {
   int st = validate<T>(d, n, ld, inf);
   if (st != APSP_OK) return st;
   const int64_t nb = n == 0 ? 0 : (n + kB - 1) / kB;
@@ -1041,23 +1078,25 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
     // double issue rate needs several waves per SIMD); smaller matrices stay in
     // int32 and skip the scan.  The scan result lives in a few bytes of
     // stream-ordered scratch; without it the call stays in int32.
-    int32_t* scratch = nullptr;
+    int32_t* scan_buf = nullptr;
     const int64_t tiles = (nb - 1) * (nb - 1);
     const int policy = g_int32_arith.load(std::memory_order_relaxed);
     const bool try_f32 = policy == APSP_ARITH_F32_WHEN_EXACT ||
                          (policy == APSP_ARITH_AUTO && tiles >= (int64_t)kP3PerCu * device_cus());
     if (try_f32) {
-      if (hipMallocAsync(reinterpret_cast<void**>(&scratch), 256, s) != hipSuccess) {
-        scratch = nullptr;
+      if (fixed_scan_buf) {
+        scan_buf = fixed_scan_buf;
+      } else if (hipMallocAsync(reinterpret_cast<void**>(&scan_buf), 256, s) != hipSuccess) {
+        scan_buf = nullptr;
         (void)hipGetLastError();
       }
     }
-    if (vec) enqueue_i32<true>(d, n, ld, inf, r0, r1, s, scratch, tm);
-    else enqueue_i32<false>(d, n, ld, inf, r0, r1, s, scratch, tm);
-    if (scratch) {
+    if (vec) enqueue_i32<true>(d, n, ld, inf, r0, r1, s, scan_buf, tm);
+    else enqueue_i32<false>(d, n, ld, inf, r0, r1, s, scan_buf, tm);
+    if (scan_buf) {
       if (scan_out)
-        (void)hipMemcpyAsync(scan_out, scratch, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
-      (void)hipFreeAsync(scratch, s);
+        (void)hipMemcpyAsync(scan_out, scan_buf, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+      if (scan_buf != fixed_scan_buf) (void)hipFreeAsync(scan_buf, s);
     }
   } else {
     (void)scan_out;
@@ -1279,6 +1318,17 @@ int apsp_fw_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream) {
 int apsp_fw_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
   const int64_t nb = n > 0 ? (n + kB - 1) / kB : 0;
   return run<float>(d, n, ld, inf, 0, nb, stream, nullptr, nullptr);
+}
+
+int apsp_fw_i32_noalloc(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream) {
+  int st = validate<int32_t>(d, n, ld, inf);
+  if (st != APSP_OK || n == 0) return st;
+  if ((st = check_device()) != APSP_OK) return st;
+  static_assert(2 <= kNoAllocScratchWords, "the scan result fits the static scratch");
+  int32_t* sc = nullptr;
+  if ((st = noalloc_scratch(&sc)) != APSP_OK) return st;
+  const int64_t nb = (n + kB - 1) / kB;
+  return run<int32_t>(d, n, ld, inf, 0, nb, stream, nullptr, nullptr, sc);
 }
 
 int apsp_fw_rounds_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t round_begin,

@@ -81,6 +81,23 @@ enum {
 int apsp_fw_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, results and arguments as apsp_fw_i32, with no allocation of
+ * any kind.  The int32 call's scan result (8 bytes) lives in a static
+ * 256-byte device array of the library instead of stream-ordered scratch;
+ * the need is 8 bytes whatever n, so no input is too large for it.  Each
+ * GPU holds one copy of that array from the first call on it until the
+ * process ends, and every call on that GPU shares it: each call clears it
+ * (with a kernel) before use, and calls that overlap in time on one GPU
+ * (different streams, or other host threads) race on it and must be
+ * serialised by the caller.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress); a failure there returns
+ * APSP_ERR_LAUNCH.  Other errors as for apsp_fw_i32.
+ */
+int apsp_fw_i32_noalloc(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream);
+
+/*
  * All-pairs shortest paths on a float32 matrix, in place (all rounds).
  * Arithmetic: IEEE binary32 add (round to nearest even) and min.
  * inf must be > 0 and not NaN; +infinity is allowed.

@@ -68,6 +68,7 @@ FAKE = 0x10000  # never dereferenced: every case below is rejected first
 ])
 def test_i32_argument_errors(lib, args):
     assert ga.apsp_fw_i32(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+    assert ga.apsp_fw_i32_noalloc(*args, 0) == ga.APSP_ERR_INVALID_VALUE
 
 
 @pytest.mark.parametrize("inf", [0.0, -1.0, float("nan"), -float("inf")])
@@ -121,6 +122,7 @@ def test_arith_policy_setter(lib):
 
 def test_empty_is_a_no_op(lib):
     assert ga.apsp_fw_i32(0, 0, 1, 100, 0) == ga.APSP_OK
+    assert ga.apsp_fw_i32_noalloc(0, 0, 1, 100, 0) == ga.APSP_OK
     assert ga.apsp_fw_f32(0, 0, 1, 1.0, 0) == ga.APSP_OK
     assert ga.apsp_fw_rounds_i32(FAKE, 300, 300, 100, 1, 1) == ga.APSP_OK
 
