@@ -549,6 +549,13 @@ def bench_host(args) -> int:
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+    # Give the pinned host blocks back while the HIP runtime is whole: torch's
+    # pinned-memory cache would otherwise free them from a static destructor
+    # at process exit.
+    del pristine, work
+    torch.cuda.synchronize()
+    if hasattr(torch._C, "_host_emptyCache"):
+        torch._C._host_emptyCache()
     return 0
 
 
@@ -795,6 +802,9 @@ def main() -> int:
     ap.add_argument("--ld", type=int, default=None, help="leading dimension (default n)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--int32-arith", choices=("auto", "f32", "int32"), default="auto",
+                    help="arithmetic policy of int32 calls: auto (default), binary32 when exact, "
+                         "or int32 forced")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -824,6 +834,10 @@ def main() -> int:
         return bench_shard(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    policy = {"auto": ga.APSP_ARITH_AUTO, "f32": ga.APSP_ARITH_F32_WHEN_EXACT,
+              "int32": ga.APSP_ARITH_INT32}[args.int32_arith]
+    if ga.apsp_set_int32_arith(policy) != ga.APSP_OK:
+        raise RuntimeError("apsp_set_int32_arith failed")
 
     spec = gg.WORKLOADS[args.workload]
     t0 = time.perf_counter()
@@ -907,7 +921,10 @@ def main() -> int:
     p3_ms_avg = phase_ms[2] / max(p3_launch, 1)
     relax_per_launch = p3_relax / max(p3_launch, 1)
     achieved = relax_per_launch / (p3_ms_avg * 1e-3) if p3_ms_avg > 0 else 0.0
-    traffic = read_traffic(args.workload, relax_per_launch)
+    # Counter summaries are kept per workload and, when the policy is not the
+    # default, per forced arithmetic.
+    profile_key = args.workload + ("" if args.int32_arith == "auto" else f"-{args.int32_arith}arith")
+    traffic = read_traffic(profile_key, relax_per_launch)
     peak = PEAK_RELAX["int32" if arith == "int32" else "f32"]
     roofline = {
         "bound": "alu",
@@ -960,6 +977,7 @@ def main() -> int:
             "workload": args.workload,
             "n": n, "ld": ld, "seed": spec["seed"], "pivot_block": B, "rounds": nb,
             "matrix_dtype": "int32" if is_int else "f32",
+            "int32_arith_policy": args.int32_arith,
             "input_sha256": sha,
         },
         "ms_per_step_by_kind": dict(zip(["phase1", "phase2", "phase3", "scan_convert"],

@@ -33,6 +33,7 @@ Tensor convenience:
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -62,7 +63,7 @@ EXPORTS = (
     "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
     "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_fw_host_plan", "apsp_successors_i32",
     "apsp_successors_f32", "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
-    "apsp_fw_i32_noalloc",
+    "apsp_fw_i32_noalloc", "apsp_release_events",
 )
 
 _lib = None
@@ -137,6 +138,7 @@ def load(path: str | None = None):
         "apsp_johnson_timed_i32": ([vp, vp, vp, i64, i64, vp, i64, i32, vp, i32, vp, dp, lp],
                                    ctypes.c_int),
         "apsp_set_int32_arith": ([ctypes.c_int], ctypes.c_int),
+        "apsp_release_events": ([], ctypes.c_int),
         "apsp_get_int32_arith": ([], ctypes.c_int),
         "apsp_minplus_ceiling": ([ctypes.c_int, dp], ctypes.c_int),
         "apsp_pivot_block": ([i64], i64),
@@ -150,7 +152,18 @@ def load(path: str | None = None):
         f.restype = res
     if path is None:
         _lib = lib
+        # Pooled timing events go back before interpreter shutdown, while the
+        # HIP runtime is whole (Python exit handlers run before the static
+        # destructors of the runtime and of torch).
+        atexit.register(_release_at_exit, lib)
     return lib
+
+
+def _release_at_exit(lib) -> None:
+    try:
+        lib.apsp_release_events()
+    except Exception:  # noqa: BLE001 - nothing to report at exit
+        pass
 
 
 # ---- raw C-ABI mirrors ------------------------------------------------------
@@ -291,6 +304,10 @@ def apsp_fw_timed_i32(d_ptr, n, ld, inf, stream=0):
 
 def apsp_fw_timed_f32(d_ptr, n, ld, inf, stream=0):
     return _timed(load().apsp_fw_timed_f32, d_ptr, n, ld, inf, stream)
+
+
+def apsp_release_events() -> int:
+    return int(load().apsp_release_events())
 
 
 def apsp_set_int32_arith(mode: int) -> int:

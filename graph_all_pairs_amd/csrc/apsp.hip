@@ -141,6 +141,8 @@ __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t
 
 // Loads the C tile into acc and applies acc <- min(acc, A (x) B) over the kB
 // pivots of block kb0; acc stays in registers (the caller stores it).
+// Per pair of pivots each accumulator takes one mp_relax2 (two adds, one
+// three-input min).
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t n, int64_t ld,
                                                T inf, int64_t row0, int64_t col0, int64_t kb0,
@@ -237,7 +239,7 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
       for (int i = 0; i < RM; ++i)
 #pragma unroll
         for (int j = 0; j < RN; ++j)
-          acc[i][j] = mp_min3(acc[i][j], a0[i] + b0[j], a1[i] + b1[j]);
+          acc[i][j] = mp_relax2(acc[i][j], a0[i], b0[j], a1[i], b1[j]);
     }
     if (c + 1 < kChunks) stash(buf ^ 1);
     __syncthreads();
@@ -1109,7 +1111,10 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
 // Timing events are created once per thread and device and reused, so the
 // measured calls do not pay for event creation.  Timing-only events carry
 // no system-scope fence (no cache writeback between the kernels they
-// bracket).  They live until the process ends.
+// bracket).  They live until apsp_release_events() on the owning thread (the
+// Python binding calls it at interpreter exit); no static destructor makes a
+// HIP call, so nothing of the library runs after the HIP runtime has begun
+// to shut down.
 struct EventPool {
   hipEvent_t* ev = nullptr;
   int64_t size = 0;
@@ -1402,6 +1407,36 @@ int apsp_trace_end(double* phase_ms, int64_t* phase_launch, int64_t* dropped) {
   }
   if (dropped) *dropped = g_trace.dropped;
   if (cur != g_trace.dev) (void)hipSetDevice(cur);
+  return rc;
+}
+
+int apsp_release_events(void) {
+  if (g_trace.on) return APSP_ERR_INVALID_VALUE;
+  bool any = false;
+  for (int dev = 0; dev < kMaxDevices; ++dev)
+    any = any || g_event_pool[dev].size > 0 || g_trace_pool[dev].size > 0;
+  delete[] g_trace.kind;
+  g_trace = Trace{};
+  if (!any) return APSP_OK;  // nothing pooled: no HIP call at all
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  int rc = APSP_OK;
+  for (EventPool* pools : {g_event_pool, g_trace_pool}) {
+    for (int dev = 0; dev < kMaxDevices; ++dev) {
+      EventPool& p = pools[dev];
+      if (p.size == 0) continue;
+      if (hipSetDevice(dev) != hipSuccess) {
+        rc = hip_failed();
+        continue;
+      }
+      for (int64_t i = 0; i < p.size; ++i)
+        if (hipEventDestroy(p.ev[i]) != hipSuccess && rc == APSP_OK) rc = hip_failed();
+      delete[] p.ev;
+      p.ev = nullptr;
+      p.size = 0;
+    }
+  }
+  if (have_cur) (void)hipSetDevice(cur);
   return rc;
 }
 

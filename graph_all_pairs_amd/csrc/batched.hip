@@ -170,7 +170,7 @@ fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t
             const T a1 = mp_min(base[128 + lr * 16 + ri], mp_add(a0, d_t_t1));
 #pragma unroll
             for (int cj = 0; cj < R; ++cj)
-              acc[ri][cj] = mp_min3(acc[ri][cj], mp_add(a0, b0[cj]), mp_add(a1, b1[cj]));
+              acc[ri][cj] = mp_relax2(acc[ri][cj], a0, b0[cj], a1, b1[cj]);
           }
           buf ^= 1;
           if (c < 3) {

@@ -37,18 +37,30 @@ __device__ __forceinline__ uint32_t ceil_min3(uint32_t a, uint32_t b, uint32_t c
   return r;
 }
 
-// A candidate sum: wrapping for int32 (VOP3 form) and binary32, saturating for the
-// unsigned packed (sum, index) keys of the successor product.
+// A candidate sum: binary32, or saturating for the unsigned packed
+// (sum, index) keys of the successor product.
 template <typename T>
 __device__ __forceinline__ T ceil_add(T a, T b) {
   if constexpr (std::is_same_v<T, uint32_t>) {
     return __builtin_elementwise_add_sat(a, b);
-  } else if constexpr (std::is_same_v<T, int32_t>) {
-    T r;  // the tile kernels' form: the wrapping add in its VOP3 encoding
-    asm("v_add_u32_e64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
   } else {
     return a + b;
+  }
+}
+
+// One accumulator over two candidates, in the tile kernels' instruction
+// order: for int32 the two VOP3 adds and the v_min3_i32 are issued in
+// sequence (as the kernels' volatile sequence does); otherwise as written.
+template <typename T>
+__device__ __forceinline__ T ceil_relax2(T acc, T a0, T b0, T a1, T b1) {
+  if constexpr (std::is_same_v<T, int32_t>) {
+    int32_t t0, t1, r;
+    asm volatile("v_add_u32_e64 %0, %1, %2" : "=v"(t0) : "v"(a0), "v"(b0));
+    asm volatile("v_add_u32_e64 %0, %1, %2" : "=v"(t1) : "v"(a1), "v"(b1));
+    asm volatile("v_min3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(acc), "v"(t0), "v"(t1));
+    return r;
+  } else {
+    return ceil_min3(acc, ceil_add(a0, b0), ceil_add(a1, b1));
   }
 }
 
@@ -72,7 +84,7 @@ minplus_core(T* __restrict__ out, int iters) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = ceil_min3(acc[i][j], ceil_add(a0[i], b0[j]), ceil_add(a1[i], b1[j]));
+      for (int j = 0; j < 8; ++j) acc[i][j] = ceil_relax2(acc[i][j], a0[i], b0[j], a1[i], b1[j]);
   }
   T s = 0;
 #pragma unroll

@@ -187,7 +187,7 @@ __device__ __forceinline__ void gemm_tile(T* __restrict__ C, int64_t ldc, const 
       for (int i = 0; i < kR; ++i)
 #pragma unroll
         for (int j = 0; j < kR; ++j)
-          acc[i][j] = mp_min3(acc[i][j], mp_add(a0[i], b0[j]), mp_add(a1[i], b1[j]));
+          acc[i][j] = mp_relax2(acc[i][j], a0[i], b0[j], a1[i], b1[j]);
     }
     if (c + 1 < chunks) stash(buf ^ 1);
     __syncthreads();

@@ -411,6 +411,18 @@ int apsp_johnson_timed_i32(const int64_t *row_ptr, const int32_t *col, const int
                            int64_t *counts);
 
 /*
+ * Destroys the HIP timing events that the measurement entry points
+ * (apsp_fw_timed_*, apsp_trace_begin) keep pooled for the calling thread,
+ * on every device, and frees their host arrays.  Later measurement calls
+ * create them again.  Call it before the HIP runtime shuts down (for
+ * example from an exit handler that runs before static destructors); the
+ * library itself makes no HIP call from a static destructor.  Returns
+ * APSP_ERR_INVALID_VALUE while a launch trace is open, APSP_ERR_LAUNCH if a
+ * HIP call failed (the events are then released as far as possible).
+ */
+int apsp_release_events(void);
+
+/*
  * Arithmetic policy of int32 calls (process-wide; affects calls made after
  * it is set).  APSP_ARITH_AUTO (default): binary32 when it is exact (see
  * above) and Phase 3 has at least two 128 x 128 tiles per compute unit,

@@ -120,6 +120,13 @@ def test_arith_policy_setter(lib):
     assert ga.apsp_get_int32_arith() == ga.APSP_ARITH_AUTO
 
 
+def test_release_events_without_pooled_events_is_a_no_op(lib):
+    # nothing is pooled in a process that made no measurement call, so the
+    # call returns at once (no HIP call, works without a GPU)
+    assert ga.apsp_release_events() == ga.APSP_OK
+    assert ga.apsp_release_events() == ga.APSP_OK
+
+
 def test_empty_is_a_no_op(lib):
     assert ga.apsp_fw_i32(0, 0, 1, 100, 0) == ga.APSP_OK
     assert ga.apsp_fw_i32_noalloc(0, 0, 1, 100, 0) == ga.APSP_OK

@@ -207,6 +207,26 @@ def test_timed_variant_counts_launches(torch_dev):
     assert cnt == [1, 3, 3, 0] and arith == 1
 
 
+def test_release_events_then_measure_again(torch_dev):
+    """The pooled timing events (timed calls and the launch trace) can be
+    released and are created again by the next measurement call."""
+    torch, dev = torch_dev
+    w = gg.erdos_renyi(300, 0.05, 1, 100, 6)
+    want = oracle.fw_i32(w)
+    for _ in range(2):
+        t = torch.from_numpy(w).to(dev)
+        ms, cnt, arith = ga.fw_timed(t, INF)
+        assert cnt[2] == 3 and np.array_equal(t.cpu().numpy(), want)
+        assert ga.apsp_trace_begin(64) == ga.APSP_OK
+        assert ga.apsp_release_events() == ga.APSP_ERR_INVALID_VALUE   # a trace is open
+        t = torch.from_numpy(w).to(dev)
+        ga.fw(t, INF)
+        st, phase_ms, launches, dropped = ga.apsp_trace_end()
+        assert st == ga.APSP_OK and launches[2] == 3 and dropped == 0
+        assert np.array_equal(t.cpu().numpy(), want)
+        assert ga.apsp_release_events() == ga.APSP_OK
+
+
 # ---- int32 matrices: binary32 vs int32 arithmetic --------------------------
 
 LIM = 1 << 24
