@@ -74,6 +74,12 @@ MUTANTS = {
                      "        if (cand < c[i * ldc + j] || t == 0) c[i * ldc + j] = cand;\n      }\n    }\n}\n\nvoid oracle_minplus_f64"),
     "mp_last_t_skipped": ("    for (int64_t t = 0; t < k; ++t) {\n      const int64_t ait",
                           "    for (int64_t t = 0; t < k - 1; ++t) {\n      const int64_t ait"),
+    "mp64_transposed_b": ("const double cand = ait + b[t * ldb + j];",
+                          "const double cand = ait + b[j * ldb + t];"),
+    "mp64_last_t_skipped": ("    for (int64_t t = 0; t < k; ++t) {\n      const double ait",
+                            "    for (int64_t t = 0; t < k - 1; ++t) {\n      const double ait"),
+    "mp64_max_not_min": ("if (cand < c[i * ldc + j]) c[i * ldc + j] = cand;\n      }\n    }\n}\n\n/*",
+                         "if (cand > c[i * ldc + j]) c[i * ldc + j] = cand;\n      }\n    }\n}\n\n/*"),
     "mp_guard_dropped": ("      if (ait == inf) continue;\n      for (int64_t j = 0; j < n; ++j) {\n        const int64_t btj",
                          "      for (int64_t j = 0; j < n; ++j) {\n        const int64_t btj"),
 }
@@ -178,6 +184,19 @@ def _battery_minplus(o: oracle.Oracle) -> None:
         for _ in range(int(np.ceil(np.log2(n - 1))) if n > 2 else 1):
             d = o.minplus(d, d, d.copy(), INF)
         assert np.array_equal(d, o.fw_i32(w).astype(np.int64))
+    # binary64: the hand-worked float product and squaring to the closure
+    fa = np.array([[0.5, 0.25, np.inf], [1.5, np.inf, 0.125]])
+    fb = np.array([[0.75, np.inf], [0.5, 2.0], [4.0, 0.375]])
+    fc = np.array([[1.0, 2.5], [np.inf, np.inf]])
+    assert o.minplus(fc, fa, fb).tolist() == [[0.75, 2.25], [2.25, 0.5]]
+    for _ in range(3):
+        n = int(rng.integers(3, 40))
+        w = np.where(rng.random((n, n)) < 0.2, rng.integers(1, 64, (n, n)) / 8.0, np.inf)
+        np.fill_diagonal(w, 0.0)
+        d = w.copy()
+        for _ in range(int(np.ceil(np.log2(n - 1))) if n > 2 else 1):
+            d = o.minplus(d, d, d.copy())
+        assert np.array_equal(d, o.fw_f64(w))
 
 
 def _battery_successors(o: oracle.Oracle) -> None:

@@ -477,6 +477,36 @@ def test_minplus_squaring_reaches_the_floyd_warshall_closure(orc, seed):
     assert np.array_equal(d, orc.fw_i32(w).astype(np.int64))
 
 
+def test_minplus_float_hand_example(orc):
+    # worked by hand with binary fractions (every sum exact in binary64), a
+    # "no path" +inf on each side, and C keeping nothing but its own +inf
+    a = np.array([[0.5, 0.25, np.inf], [1.5, np.inf, 0.125]])
+    b = np.array([[0.75, np.inf], [0.5, 2.0], [4.0, 0.375]])
+    c = np.array([[1.0, 2.5], [np.inf, np.inf]])
+    got = orc.minplus(c, a, b)
+    # (0,0): min(1.0, 0.5+0.75, 0.25+0.5) = 0.75    (0,1): min(2.5, 0.25+2.0) = 2.25
+    # (1,0): min(1.5+0.75, 0.125+4.0) = 2.25        (1,1): min(0.125+0.375) = 0.5
+    assert got.tolist() == [[0.75, 2.25], [2.25, 0.5]]
+    # C is kept where the product cannot beat it
+    assert orc.minplus(np.array([[0.5]]), np.array([[0.25]]), np.array([[0.5]])).tolist() == [[0.5]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_minplus_float_squaring_reaches_the_floyd_warshall_closure(orc, seed):
+    # binary64 weights that are multiples of 1/8 below 8: every path sum is
+    # exact, so ceil(log2(n - 1)) squarings equal the pinned plain recurrence
+    # bit for bit
+    rng = np.random.default_rng(950 + seed)
+    n = int(rng.integers(2, 60))
+    w = np.where(rng.random((n, n)) < [0.08, 0.3][seed % 2],
+                 rng.integers(1, 64, (n, n)) / 8.0, np.inf)
+    np.fill_diagonal(w, 0.0)
+    d = w.copy()
+    for _ in range(max(1, int(np.ceil(np.log2(max(n - 1, 2)))))):
+        d = orc.minplus(d, d, d.copy())
+    assert np.array_equal(d, orc.fw_f64(w))
+
+
 def test_minplus_float_with_ieee_inf(orc):
     rng = np.random.default_rng(8)
     m, n, k = 20, 25, 30
