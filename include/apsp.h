@@ -257,8 +257,16 @@ int apsp_fw_host_plan(int64_t n, int64_t elem_bytes, int64_t device_bytes, int64
  *            output);
  *   nxt, ldn device int32 output, n x n, ldn >= n.
  * Pointers 4-byte aligned (128-bit loads when w and d are 16-byte aligned and
- * ldw, ldd are multiples of 4).  Following nxt from i reaches j along a path
- * whose weights sum to d[i][j] when every weight on it is positive.
+ * ldw, ldd are multiples of 4).
+ * Precondition for walkable successors: no cycle of total weight 0 (with
+ * weights >= 0, a cycle of 0-weight edges).  Then following nxt from i
+ * reaches j within n - 1 hops along a path whose weights sum to d[i][j]:
+ * each hop keeps d(., j) + the weight walked constant and d(., j) never
+ * increases, so a vertex seen twice would close a 0-weight cycle.  With
+ * such a cycle the matrix is still the one defined above (ties go to the
+ * smallest u), but two vertices of the cycle can name each other as first
+ * hop towards the same j, and apsp_path then returns -3 for the pairs whose
+ * walk enters that loop.
  * Work: n^3 candidates when w has more than n^2/16 finite off-diagonal
  * entries; else only the neighbours of each i are tried (n candidates per
  * edge).  For n^3 candidates in int32, when every finite weight and distance
@@ -289,7 +297,8 @@ int apsp_fw_paths_f32(float *d, int64_t ld, int32_t *nxt, int64_t ldn, int64_t n
  * first): writes the vertices i, ..., j into path[0 .. min(len, cap)) and
  * returns len, the number of vertices (1 when i = j).  Returns -1 when j is
  * unreachable from i, -2 for bad arguments, -3 when the successors do not
- * reach j within n hops (a zero-weight cycle).  Host code only.
+ * reach j within n hops (possible only when the graph has a cycle of total
+ * weight 0; see apsp_successors_*).  Host code only.
  */
 int64_t apsp_path(const int32_t *nxt, int64_t ldn, int64_t n, int64_t i, int64_t j,
                   int32_t *path, int64_t cap);

@@ -182,3 +182,74 @@ def test_successors_on_the_complete_workload_shape(dev, orc):
     d = orc.fw_i32(w)
     got = gpu_successors(dev, w, d)
     assert np.array_equal(got, orc.successors(w, d, INF))
+
+
+# ---- zero-weight cycles ------------------------------------------------------
+# Weights may be 0, so two vertices joined by 0-weight edges both ways can tie
+# as first hops towards the same target.  The successor matrix is still the
+# defined one (smallest minimising u, equal to the oracle's), but following it
+# may loop: apsp_path then returns -3.  Without a cycle of total weight 0 every
+# walk reaches its target.
+
+def walk_expected(nxt, i, j):
+    """What the host walker must return for (i, j): the vertex count of the
+    walk, -1 when j is unreachable, -3 when the walk does not reach j within
+    n hops (it entered a successor cycle)."""
+    n = nxt.shape[0]
+    if nxt[i, j] < 0:
+        return -1
+    v, count = i, 1
+    for _ in range(n):
+        if v == j:
+            return count
+        v = int(nxt[v, j])
+        count += 1
+    return count if v == j else -3
+
+
+def zero_cycle_graph(n, p, seed, a, b):
+    """Sparse or dense integer weights 1..9 with a 0-weight 2-cycle a <-> b,
+    a < every other vertex: a's only out-edge goes to b.  For every j that
+    b reaches, a's first hop is b (its one candidate) and b's is a (0 +
+    d(a, j) = d(b, j), and a is the smallest index), so the two name each
+    other."""
+    w = gg.erdos_renyi(n, p, 1, 9, seed)
+    w[a, :] = INF
+    w[a, a] = w[b, b] = 0
+    w[a, b] = w[b, a] = 0
+    return w
+
+
+# (n, p, scale): dense packed keys, the neighbour lists (p = 0.02), and with
+# weights scaled by 2^21 the dense (value, index) kernel (the keys no longer
+# fit 32 bits at n = 300).
+@pytest.mark.parametrize("n,p,scale", [(6, 0.9, 1), (64, 0.3, 1), (200, 0.02, 1), (300, 0.5, 1),
+                                       (300, 0.5, 1 << 21)])
+def test_zero_weight_two_cycle(dev, orc, n, p, scale):
+    print(f"case successors with a zero-weight 2-cycle n={n} p={p} scale={scale}", flush=True)
+    a, b = 0, n - 2
+    w = zero_cycle_graph(n, p, 700 + n, a, b)
+    w = np.where(w == INF, INF, w.astype(np.int64) * scale).astype(np.int32)
+    d = orc.fw_i32(w)
+    want = orc.successors(w, d, INF)
+    got = gpu_successors(dev, w, d)
+    assert np.array_equal(got, want)
+    # the 2-cycle is real: some target has a and b naming each other
+    loops = [j for j in range(n) if j not in (a, b) and want[a, j] == b and want[b, j] == a]
+    assert loops, "the graph does not exercise the zero-weight cycle"
+    buf = np.empty(n + 1, dtype=np.int32)
+    g = np.ascontiguousarray(got)
+    for i in range(n):
+        for j in range(n):
+            r = ga.apsp_path(g.ctypes.data, n, n, i, j, buf.ctypes.data, len(buf))
+            assert r == walk_expected(want, i, j), (i, j, r)
+            if r > 0:   # a finished walk has the shortest distance's weight
+                hops = buf[:r]
+                assert hops[0] == i and hops[-1] == j
+                assert int(sum(int(w[x, y]) for x, y in zip(hops[:-1], hops[1:]))) == int(d[i, j])
+    for j in loops:
+        assert ga.apsp_path(g.ctypes.data, n, n, a, j, buf.ctypes.data, len(buf)) == -3
+    # float32 takes the same definition (weights are small integers, exact)
+    wf = np.where(w == INF, np.float32(np.inf), w.astype(np.float32)).astype(np.float32)
+    df = np.where(d == INF, np.float32(np.inf), d.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(gpu_successors(dev, wf, df), want)
