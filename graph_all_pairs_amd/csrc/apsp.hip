@@ -99,10 +99,11 @@ struct TileShape {
 // C tile <-> registers, in the micro-tile layout described above.
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void load_tile(const T* __restrict__ d, int64_t n, int64_t ld, T inf,
-                                          int64_t row0, int64_t col0, T (&acc)[RM][RN]) {
+                                          int64_t row0, int64_t col0, T (&acc)[RM][RN],
+                                          int tid = threadIdx.x) {
   using S = TileShape<T, TM, TN, RM, RN>;
-  const int tc = threadIdx.x % S::kThrCols;
-  const int tr = threadIdx.x / S::kThrCols;
+  const int tc = tid % S::kThrCols;
+  const int tr = tid / S::kThrCols;
 #pragma unroll
   for (int gi = 0; gi < RM / 4; ++gi)
 #pragma unroll
@@ -120,10 +121,11 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ d, int64_t n, in
 
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t ld,
-                                           int64_t row0, int64_t col0, const T (&acc)[RM][RN]) {
+                                           int64_t row0, int64_t col0, const T (&acc)[RM][RN],
+                                           int tid = threadIdx.x) {
   using S = TileShape<T, TM, TN, RM, RN>;
-  const int tc = threadIdx.x % S::kThrCols;
-  const int tr = threadIdx.x / S::kThrCols;
+  const int tc = tid % S::kThrCols;
+  const int tr = tid / S::kThrCols;
 #pragma unroll
   for (int gi = 0; gi < RM / 4; ++gi)
 #pragma unroll
@@ -143,15 +145,19 @@ __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t
 // pivots of block kb0; acc stays in registers (the caller stores it).
 // Per pair of pivots each accumulator takes one mp_relax2 (two adds, one
 // three-input min).
+// Chunks c_begin .. c_begin + c_count - 1 of kKC pivots are applied (all
+// kB pivots by default); tid is the thread's index within the 256 threads
+// that share `lds`.  Ends with a barrier after its last LDS reads.
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t n, int64_t ld,
                                                T inf, int64_t row0, int64_t col0, int64_t kb0,
-                                               T* __restrict__ lds, T (&acc)[RM][RN]) {
+                                               T* __restrict__ lds, T (&acc)[RM][RN],
+                                               int c_begin = 0, int c_count = kB / kKC,
+                                               int tid = threadIdx.x) {
   using S = TileShape<T, TM, TN, RM, RN>;
   T* sA = lds;                              // [2][kKC][kLdA]
   T* sB = lds + 2 * kKC * S::kLdA;          // [2][kKC][kLdB]
 
-  const int tid = threadIdx.x;
   const int tc = tid % S::kThrCols;
   const int tr = tid / S::kThrCols;
 
@@ -200,16 +206,15 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
     }
   };
 
-  fetch(0);
-  load_tile<T, TM, TN, RM, RN, VEC, EDGE>(d, n, ld, inf, row0, col0, acc);
+  fetch(c_begin);
+  load_tile<T, TM, TN, RM, RN, VEC, EDGE>(d, n, ld, inf, row0, col0, acc, tid);
   stash(0);
   __syncthreads();
 
-  constexpr int kChunks = kB / kKC;
 #pragma unroll 1
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < c_count; ++c) {
     const int buf = c & 1;
-    if (c + 1 < kChunks) fetch(c + 1);
+    if (c + 1 < c_count) fetch(c_begin + c + 1);
     const T* a = sA + buf * kKC * S::kLdA;
     const T* b = sB + buf * kKC * S::kLdB;
 #pragma unroll
@@ -241,25 +246,11 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
         for (int j = 0; j < RN; ++j)
           acc[i][j] = mp_relax2(acc[i][j], a0[i], b0[j], a1[i], b1[j]);
     }
-    if (c + 1 < kChunks) stash(buf ^ 1);
+    if (c + 1 < c_count) stash(buf ^ 1);
     __syncthreads();
   }
 }
 
-template <typename T, int TM, int TN, int RM, int RN, bool VEC>
-__device__ __forceinline__ void minplus_tile(T* __restrict__ d, int64_t n, int64_t ld, T inf,
-                                             int64_t row0, int64_t col0, int64_t kb0,
-                                             T* __restrict__ lds) {
-  T acc[RM][RN];
-  const bool interior = row0 + TM <= n && col0 + TN <= n && kb0 + kB <= n;
-  if (interior) {
-    minplus_update<T, TM, TN, RM, RN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc);
-    store_tile<T, TM, TN, RM, RN, VEC, false>(d, n, ld, row0, col0, acc);
-  } else {
-    minplus_update<T, TM, TN, RM, RN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc);
-    store_tile<T, TM, TN, RM, RN, VEC, true>(d, n, ld, row0, col0, acc);
-  }
-}
 
 // Phase-2 panel tiles: the row panel is split into kB x kP2 tiles, the column
 // panel into kP2 x kB tiles.
@@ -383,7 +374,61 @@ __device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_
 
 // ---------------------------------------------------------------------------
 // Phase 2: pivot-row tiles (blocks 0 .. nr-1) then pivot-column tiles.
+//
+// A Phase-2 piece (kB x kP2 or kP2 x kB, kB pivots) has too little work per
+// thread for its 4 x 4 micro-tile to keep the VALU fed: 2048 relaxations
+// per thread in a row, two waves per SIMD.  So each 512-thread workgroup
+// splits the pivot depth between its two halves: threads 0-255 apply pivot
+// chunks 0-3, threads 256-511 chunks 4-7, each half from its own LDS
+// buffers and starting from the same tile.  The second half then hands its
+// accumulators over LDS and the first stores the elementwise minimum, which
+// is min(C, A (x) B) over all kB pivots (min is exact and order-free, so the
+// result is the same bit for bit as one half applying all pivots).
 // ---------------------------------------------------------------------------
+constexpr int kP2Threads = 2 * kThreads;
+template <typename T, int TM, int TN, bool VEC, bool EDGE>
+__device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                          int64_t row0, int64_t col0, int64_t kb0,
+                                          T* __restrict__ lds) {
+  using S = TileShape<T, TM, TN, 4, 4>;
+  constexpr int kHalf = kB / kKC / 2;  // chunks per half
+  const int half = threadIdx.x / kThreads;
+  const int tid = threadIdx.x % kThreads;
+  T acc[4][4];
+  minplus_update<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, inf, row0, col0, kb0,
+                                             lds + half * S::kLdsElems, acc, half * kHalf, kHalf,
+                                             tid);
+  // Both halves passed minplus_update's final barrier: the LDS is free.
+  constexpr int kLdR = TN + kPad;
+  static_assert(TM * kLdR <= 2 * S::kLdsElems, "the hand-over fits the LDS");
+  const int tc = tid % S::kThrCols, tr = tid / S::kThrCols;
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store4(lds + (tr * 4 + i) * kLdR + tc * 4, acc[i]);
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      T v[4];
+      load4(lds + (tr * 4 + i) * kLdR + tc * 4, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mp_min(acc[i][j], v[j]);
+    }
+    store_tile<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, row0, col0, acc, tid);
+  }
+}
+
+template <typename T, int TM, int TN, bool VEC>
+__device__ __forceinline__ void p2_piece(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                         int64_t row0, int64_t col0, int64_t kb0,
+                                         T* __restrict__ lds) {
+  if (row0 + TM <= n && col0 + TN <= n && kb0 + kB <= n)
+    p2_halves<T, TM, TN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds);
+  else
+    p2_halves<T, TM, TN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds);
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, T* __restrict__ lds) {
@@ -396,14 +441,14 @@ __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_
     const int64_t J = jp + (jp >= K);
     const int64_t col0 = J * kB + sub * kP2;
     if (col0 >= n) return;
-    minplus_tile<T, kB, kP2, 4, 4, VEC>(d, n, ld, inf, kb0, col0, kb0, lds);
+    p2_piece<T, kB, kP2, VEC>(d, n, ld, inf, kb0, col0, kb0, lds);
   } else {
     b -= nr;
     const int64_t ip = b / kSub, sub = b % kSub;
     const int64_t I = ip + (ip >= K);
     const int64_t row0 = I * kB + sub * kP2;
     if (row0 >= n) return;
-    minplus_tile<T, kP2, kB, 4, 4, VEC>(d, n, ld, inf, row0, kb0, kb0, lds);
+    p2_piece<T, kP2, kB, VEC>(d, n, ld, inf, row0, kb0, kb0, lds);
   }
 }
 
@@ -635,9 +680,9 @@ __global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t
 }
 
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+__global__ void __launch_bounds__(kP2Threads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
 fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb) {
-  __shared__ __attribute__((aligned(16))) T lds[kLdsP2];
+  __shared__ __attribute__((aligned(16))) T lds[2 * kLdsP2];
   phase2_body<T, VEC>(d, n, ld, inf, K, nb, lds);
 }
 
@@ -661,10 +706,10 @@ __global__ void __launch_bounds__(kThreads) fw_phase1_i32(int32_t* __restrict__ 
 }
 
 template <bool VEC>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+__global__ void __launch_bounds__(kP2Threads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
 fw_phase2_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
               const int32_t* __restrict__ s) {
-  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP2];
+  __shared__ __attribute__((aligned(16))) int32_t lds[2 * kLdsP2];
   if (f32_exact(s, n))
     phase2_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
                             reinterpret_cast<float*>(lds));
@@ -1001,10 +1046,10 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
     mark(kKindPhase2, true);
     if constexpr (std::is_same_v<T, int32_t>)
-      hipLaunchKernelGGL((fw_phase2_i32<VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n,
+      hipLaunchKernelGGL((fw_phase2_i32<VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n,
                          ld, inf, K, nb, scan_buf);
     else
-      hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kThreads), 0, s, d, n, ld,
+      hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n, ld,
                          inf, K, nb);
     mark(kKindPhase2, false);
     const int64_t g3 = (nb - 1) * (nb - 1);
