@@ -96,11 +96,57 @@ struct TileShape {
   static constexpr int kLdsElems = 2 * kKC * (kLdA + kLdB);
 };
 
+// ---------------------------------------------------------------------------
+// An int32 matrix computed in binary32 is converted on the fly: the loads of
+// the first round read int32 entries and convert them (the sentinel becomes
+// +infinity), the stores of the last round convert back (see i32_to_f32 and
+// f32_to_i32).  The flags say which accesses of a launch convert.
+// ---------------------------------------------------------------------------
+constexpr int kConvC = 1;      // the C tile's loads
+constexpr int kConvA = 2;      // the A operand's loads (Phase 2 column pieces: the piece itself)
+constexpr int kConvB = 4;      // the B operand's loads (Phase 2 row pieces: the piece itself)
+constexpr int kConvOut = 8;    // every store of the launch
+constexpr int kConvDiag = 16;  // Phase 3 of the last round: block (K, K) goes back too
+
+// gload4, converting int32 entries to binary32 when cv is set.  Elements
+// outside the matrix read as inf32, which converts to +infinity.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void gload4x(const T* __restrict__ d, int64_t ld, int64_t n,
+                                        int64_t row, int64_t col, T inf, T (&v)[4], bool cv,
+                                        int32_t inf32) {
+  if constexpr (std::is_same_v<T, float>) {
+    if (cv) {
+      int32_t r[4];
+      gload4<int32_t, VEC, EDGE>(reinterpret_cast<const int32_t*>(d), ld, n, row, col, inf32, r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = i32_to_f32(r[e], inf32);
+      return;
+    }
+  }
+  gload4<T, VEC, EDGE>(d, ld, n, row, col, inf, v);
+}
+
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void gstore4x(T* __restrict__ d, int64_t ld, int64_t n, int64_t row,
+                                         int64_t col, const T (&v)[4], bool cv, int32_t inf32) {
+  if constexpr (std::is_same_v<T, float>) {
+    if (cv) {
+      int32_t r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = f32_to_i32(v[e], inf32);
+      gstore4<int32_t, VEC, EDGE>(reinterpret_cast<int32_t*>(d), ld, n, row, col, r);
+      return;
+    }
+  }
+  gstore4<T, VEC, EDGE>(d, ld, n, row, col, v);
+}
+
 // C tile <-> registers, in the micro-tile layout described above.
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void load_tile(const T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                           int64_t row0, int64_t col0, T (&acc)[RM][RN],
-                                          int tid = threadIdx.x) {
+                                          int tid = threadIdx.x, bool cv = false,
+                                          int32_t inf32 = 0) {
   using S = TileShape<T, TM, TN, RM, RN>;
   const int tc = tid % S::kThrCols;
   const int tr = tid / S::kThrCols;
@@ -112,7 +158,8 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ d, int64_t n, in
 #pragma unroll
       for (int gj = 0; gj < RN / 4; ++gj) {
         T v[4];
-        gload4<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, inf, v);
+        gload4x<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, inf, v, cv,
+                              inf32);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[gi * 4 + i][gj * 4 + j] = v[j];
       }
@@ -122,7 +169,8 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ d, int64_t n, in
 template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
 __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t ld,
                                            int64_t row0, int64_t col0, const T (&acc)[RM][RN],
-                                           int tid = threadIdx.x) {
+                                           int tid = threadIdx.x, bool cv = false,
+                                           int32_t inf32 = 0) {
   using S = TileShape<T, TM, TN, RM, RN>;
   const int tc = tid % S::kThrCols;
   const int tr = tid / S::kThrCols;
@@ -136,7 +184,8 @@ __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t
         T v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = acc[gi * 4 + i][gj * 4 + j];
-        gstore4<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, v);
+        gstore4x<T, VEC, EDGE>(d, ld, n, row, col0 + gj * S::kGroupColStride + tc * 4, v, cv,
+                               inf32);
       }
     }
 }
@@ -153,7 +202,8 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
                                                T inf, int64_t row0, int64_t col0, int64_t kb0,
                                                T* __restrict__ lds, T (&acc)[RM][RN],
                                                int c_begin = 0, int c_count = kB / kKC,
-                                               int tid = threadIdx.x) {
+                                               int tid = threadIdx.x, int conv = 0,
+                                               int32_t inf32 = 0) {
   using S = TileShape<T, TM, TN, RM, RN>;
   T* sA = lds;                              // [2][kKC][kLdA]
   T* sB = lds + 2 * kKC * S::kLdA;          // [2][kKC][kLdB]
@@ -172,7 +222,7 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
       const int q = tid + l * kThreads;
       if (S::kQuadsA % kThreads == 0 || q < S::kQuadsA) {
         const int r = q / (kKC / 4), kq = q % (kKC / 4);
-        gload4<T, VEC, EDGE>(d, ld, n, row0 + r, k0 + kq * 4, inf, ga[l]);
+        gload4x<T, VEC, EDGE>(d, ld, n, row0 + r, k0 + kq * 4, inf, ga[l], conv & kConvA, inf32);
       }
     }
 #pragma unroll
@@ -180,7 +230,7 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
       const int q = tid + l * kThreads;
       if (S::kQuadsB % kThreads == 0 || q < S::kQuadsB) {
         const int kr = q / (TN / 4), cq = q % (TN / 4);
-        gload4<T, VEC, EDGE>(d, ld, n, k0 + kr, col0 + cq * 4, inf, gb[l]);
+        gload4x<T, VEC, EDGE>(d, ld, n, k0 + kr, col0 + cq * 4, inf, gb[l], conv & kConvB, inf32);
       }
     }
   };
@@ -207,7 +257,8 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
   };
 
   fetch(c_begin);
-  load_tile<T, TM, TN, RM, RN, VEC, EDGE>(d, n, ld, inf, row0, col0, acc, tid);
+  load_tile<T, TM, TN, RM, RN, VEC, EDGE>(d, n, ld, inf, row0, col0, acc, tid, conv & kConvC,
+                                          inf32);
   stash(0);
   __syncthreads();
 
@@ -355,20 +406,27 @@ __device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ 
   }
 }
 
-// Standalone Phase 1 (first round of a call).
+// Standalone Phase 1 (first round of a call).  conv: kConvC converts the
+// block on load, kConvOut on store.
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
-                                            int64_t K, T* __restrict__ lds) {
+                                            int64_t K, T* __restrict__ lds, int conv,
+                                            int32_t inf32) {
   const int64_t base = K * kB;
+  const int tid = threadIdx.x;
   T acc[8][8];
   if (base + kB <= n) {
-    load_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, base, base, acc);
+    load_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, base, base, acc, tid, conv & kConvC,
+                                            inf32);
     close_block<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, base, base, acc);
+    store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, base, base, acc, tid, conv & kConvOut,
+                                             inf32);
   } else {
-    load_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, base, base, acc);
+    load_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, base, base, acc, tid, conv & kConvC,
+                                           inf32);
     close_block<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, base, base, acc);
+    store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, base, base, acc, tid, conv & kConvOut,
+                                            inf32);
   }
 }
 
@@ -389,7 +447,7 @@ constexpr int kP2Threads = 2 * kThreads;
 template <typename T, int TM, int TN, bool VEC, bool EDGE>
 __device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                           int64_t row0, int64_t col0, int64_t kb0,
-                                          T* __restrict__ lds) {
+                                          T* __restrict__ lds, int conv, int32_t inf32) {
   using S = TileShape<T, TM, TN, 4, 4>;
   constexpr int kHalf = kB / kKC / 2;  // chunks per half
   const int half = threadIdx.x / kThreads;
@@ -397,7 +455,7 @@ __device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t 
   T acc[4][4];
   minplus_update<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, inf, row0, col0, kb0,
                                              lds + half * S::kLdsElems, acc, half * kHalf, kHalf,
-                                             tid);
+                                             tid, conv, inf32);
   // Both halves passed minplus_update's final barrier: the LDS is free.
   constexpr int kLdR = TN + kPad;
   static_assert(TM * kLdR <= 2 * S::kLdsElems, "the hand-over fits the LDS");
@@ -415,23 +473,29 @@ __device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t 
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mp_min(acc[i][j], v[j]);
     }
-    store_tile<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, row0, col0, acc, tid);
+    store_tile<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, row0, col0, acc, tid, conv & kConvOut,
+                                           inf32);
   }
 }
 
 template <typename T, int TM, int TN, bool VEC>
 __device__ __forceinline__ void p2_piece(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                          int64_t row0, int64_t col0, int64_t kb0,
-                                         T* __restrict__ lds) {
+                                         T* __restrict__ lds, int conv, int32_t inf32) {
   if (row0 + TM <= n && col0 + TN <= n && kb0 + kB <= n)
-    p2_halves<T, TM, TN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds);
+    p2_halves<T, TM, TN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32);
   else
-    p2_halves<T, TM, TN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds);
+    p2_halves<T, TM, TN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32);
 }
 
+// conv: kConvC converts the piece's own entries on load (as C and as its
+// operand: B of a row piece, A of a column piece; D_KK is already binary32),
+// kConvOut converts on store.
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
-                                            int64_t K, int64_t nb, T* __restrict__ lds) {
+                                            int64_t K, int64_t nb, T* __restrict__ lds, int conv,
+                                            int32_t inf32) {
+  const int own = (conv & kConvC) ? kConvC : 0;
   constexpr int kSub = kB / kP2;
   const int64_t nr = (nb - 1) * kSub;
   int64_t b = blockIdx.x;
@@ -441,14 +505,16 @@ __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_
     const int64_t J = jp + (jp >= K);
     const int64_t col0 = J * kB + sub * kP2;
     if (col0 >= n) return;
-    p2_piece<T, kB, kP2, VEC>(d, n, ld, inf, kb0, col0, kb0, lds);
+    p2_piece<T, kB, kP2, VEC>(d, n, ld, inf, kb0, col0, kb0, lds,
+                              own | (own ? kConvB : 0) | (conv & kConvOut), inf32);
   } else {
     b -= nr;
     const int64_t ip = b / kSub, sub = b % kSub;
     const int64_t I = ip + (ip >= K);
     const int64_t row0 = I * kB + sub * kP2;
     if (row0 >= n) return;
-    p2_piece<T, kP2, kB, VEC>(d, n, ld, inf, row0, kb0, kb0, lds);
+    p2_piece<T, kP2, kB, VEC>(d, n, ld, inf, row0, kb0, kb0, lds,
+                              own | (own ? kConvA : 0) | (conv & kConvOut), inf32);
   }
 }
 
@@ -485,10 +551,15 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
   return g * kBand * m + jp * rows + (ip - base);
 }
 
+// conv: kConvC converts the C tile on load, kConvA / kConvB the pivot
+// column / row operands (which the last round's Phase 2 stored as int32),
+// kConvOut the stores; kConvDiag (last round) has workgroup 0 also convert
+// block (K, K) back, which no Phase-3 workgroup reads and Phase 2 has
+// finished reading.
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, int fuse_next,
-                                            T* __restrict__ lds) {
+                                            T* __restrict__ lds, int conv, int32_t inf32) {
   const uint32_t m = (uint32_t)(nb - 1);
   const uint32_t total = m * m;
   const uint32_t b = blockIdx.x;
@@ -508,15 +579,30 @@ __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_
   const int64_t row0 = I * kB, col0 = J * kB, kb0 = K * kB;
 
   T acc[8][8];
+  const int tid = threadIdx.x;
+  const int cin = conv & (kConvC | kConvA | kConvB);
+  const bool cout = (conv & kConvOut) != 0;
   const bool interior = row0 + kB <= n && col0 + kB <= n && kb0 + kB <= n;
   if (interior) {
-    minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc);
+    minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
+                                                kB / kKC, tid, cin, inf32);
     if (special) close_block_seq<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, row0, col0, acc);
+    store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, row0, col0, acc, tid, cout, inf32);
   } else {
-    minplus_update<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc);
+    minplus_update<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
+                                               kB / kKC, tid, cin, inf32);
     if (special) close_block_seq<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, row0, col0, acc);
+    store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, row0, col0, acc, tid, cout, inf32);
+  }
+  if ((conv & kConvDiag) && b == 0) {
+    // Block (K, K) back to int32, in place (it holds binary32 bits).
+    if (kb0 + kB <= n) {
+      load_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, kb0, kb0, acc, tid);
+      store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, kb0, kb0, acc, tid, true, inf32);
+    } else {
+      load_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, kb0, kb0, acc, tid);
+      store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, kb0, kb0, acc, tid, true, inf32);
+    }
   }
 }
 
@@ -627,106 +713,70 @@ __global__ void __launch_bounds__(kThreads) scan_i32(const int32_t* __restrict__
   }
 }
 
-// In place: int32 bit patterns <-> binary32 bit patterns (only when exact).
-template <bool VEC, bool TO_F32>
-__global__ void __launch_bounds__(kThreads) convert_i32(int32_t* __restrict__ d, int64_t n,
-                                                        int64_t ld, int32_t inf,
-                                                        const int32_t* __restrict__ s) {
-  if (!f32_exact(s, n)) return;
-  auto conv = [&](int32_t v) -> int32_t {
-    if (TO_F32) return __float_as_int(i32_to_f32(v, inf));
-    return f32_to_i32(__int_as_float(v), inf);
-  };
-  const int64_t quads = (n + 3) / 4;
-  const int64_t full = VEC ? n / 4 : 0;  // quads wholly inside the row
-  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
-    int32_t* row = d + r * ld;
-    int64_t q = threadIdx.x;
-    for (; q + 3 * kThreads < full; q += 4 * kThreads) {  // four quads in flight
-      int32_t v[4][4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) load4(row + (q + k * kThreads) * 4, v[k]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[k][e] = conv(v[k][e]);
-        store4(row + (q + k * kThreads) * 4, v[k]);
-      }
-    }
-    for (; q < quads; q += kThreads) {
-      const int64_t c = q * 4;
-      if (VEC && c + 3 < n) {
-        int32_t v[4];
-        load4(row + c, v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = conv(v[e]);
-        store4(row + c, v);
-      } else {
-        for (int e = 0; e < 4 && c + e < n; ++e) row[c + e] = conv(row[c + e]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Kernels.  fw_phase* run one element type; fw_phase*_i32 serve int32
-// matrices and take the binary32 body when the call's scan says it is exact.
+// matrices and take the binary32 body when the call's scan says it is exact,
+// converting on the first round's loads and the last round's stores as
+// `conv` says (see kConvC).  Only the CONV instances convert: the rounds in
+// between run instances with no conversion code in their loops.
 // ---------------------------------------------------------------------------
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
                                                       T inf, int64_t K) {
   __shared__ __attribute__((aligned(16))) T lds[kLdsClose];
-  phase1_body<T, VEC>(d, n, ld, inf, K, lds);
+  phase1_body<T, VEC>(d, n, ld, inf, K, lds, 0, 0);
 }
 
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kP2Threads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
 fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb) {
   __shared__ __attribute__((aligned(16))) T lds[2 * kLdsP2];
-  phase2_body<T, VEC>(d, n, ld, inf, K, nb, lds);
+  phase2_body<T, VEC>(d, n, ld, inf, K, nb, lds, 0, 0);
 }
 
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
 fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next) {
   __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
-  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, lds);
+  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, lds, 0, 0);
 }
 
-template <bool VEC>
+template <bool VEC, bool CONV>
 __global__ void __launch_bounds__(kThreads) fw_phase1_i32(int32_t* __restrict__ d, int64_t n,
                                                           int64_t ld, int32_t inf, int64_t K,
+                                                          int conv,
                                                           const int32_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kLdsClose];
   if (f32_exact(s, n))
     phase1_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K,
-                            reinterpret_cast<float*>(lds));
+                            reinterpret_cast<float*>(lds), CONV ? conv : 0, inf);
   else
-    phase1_body<int32_t, VEC>(d, n, ld, inf, K, lds);
+    phase1_body<int32_t, VEC>(d, n, ld, inf, K, lds, 0, 0);
 }
 
-template <bool VEC>
+template <bool VEC, bool CONV>
 __global__ void __launch_bounds__(kP2Threads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
 fw_phase2_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
-              const int32_t* __restrict__ s) {
+              int conv, const int32_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) int32_t lds[2 * kLdsP2];
   if (f32_exact(s, n))
     phase2_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
-                            reinterpret_cast<float*>(lds));
+                            reinterpret_cast<float*>(lds), CONV ? conv : 0, inf);
   else
-    phase2_body<int32_t, VEC>(d, n, ld, inf, K, nb, lds);
+    phase2_body<int32_t, VEC>(d, n, ld, inf, K, nb, lds, 0, 0);
 }
 
-template <bool VEC>
+template <bool VEC, bool CONV>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
 fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
-              int fuse_next, const int32_t* __restrict__ s) {
+              int fuse_next, int conv, const int32_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP3];
   if (f32_exact(s, n))
     phase3_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
-                            fuse_next, reinterpret_cast<float*>(lds));
+                            fuse_next, reinterpret_cast<float*>(lds), CONV ? conv : 0,
+                            inf);
   else
-    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, lds);
+    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, lds, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -978,7 +1028,7 @@ int validate(const T* d, int64_t n, int64_t ld, T inf) {
 }
 
 // Launch kinds reported by the timed entry points.
-enum { kKindPhase1 = 0, kKindPhase2 = 1, kKindPhase3 = 2, kKindConvert = 3, kKinds = 4 };
+enum { kKindPhase1 = 0, kKindPhase2 = 1, kKindPhase3 = 2, kKindScan = 3, kKinds = 4 };
 
 struct PhaseTimer {
   // Events bracketing each launch: ev[2*i] before, ev[2*i+1] after launch i.
@@ -1024,12 +1074,32 @@ int launch_status() {
   return APSP_OK;
 }
 
+// Launches the converting instance of an int32 phase kernel when `mask`
+// asks for a conversion, else the plain one; both take (args..., conv, scan).
+template <typename K, typename... A>
+void launch_i32(K plain, K conv, int64_t grid, int threads, hipStream_t s, int mask,
+                const int32_t* scan, A... args) {
+  if (mask)
+    hipLaunchKernelGGL(conv, dim3((unsigned)grid), dim3(threads), 0, s, args..., mask, scan);
+  else
+    hipLaunchKernelGGL(plain, dim3((unsigned)grid), dim3(threads), 0, s, args..., 0, scan);
+}
+
 // Rounds [r0, r1).  For int32 matrices `scan_buf` (may be null) holds the
 // scan result that selects binary32 or int32 arithmetic inside the kernels.
+// In binary32 the matrix is converted on the way: round r0 reads every
+// block once before any other access (block (r0, r0) in Phase 1, its pivot
+// row and column in Phase 2, the rest in Phase 3), so those loads convert;
+// round r1 - 1 writes every block once after its last read, so its stores
+// convert, and Phase 3 of that round converts the pivot row and column it
+// reads (Phase 2 stored them as int32) and, in workgroup 0, block (K, K).
 template <typename T, bool VEC>
 void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
                     const int32_t* scan_buf, PhaseTimer* tm) {
   const int64_t nb = (n + kB - 1) / kB;
+  const int conv_first = scan_buf ? kConvC : 0;
+  const int conv_last = scan_buf ? kConvOut : 0;
+  const int conv_last3 = scan_buf ? kConvOut | kConvA | kConvB | kConvDiag : 0;
   auto mark = [&](int k, bool before) {
     if (tm) tm->mark(k, before);
   };
@@ -1037,8 +1107,8 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   // Phase 1 runs inside the previous round's Phase-3 launch.
   mark(kKindPhase1, true);
   if constexpr (std::is_same_v<T, int32_t>)
-    hipLaunchKernelGGL((fw_phase1_i32<VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0,
-                       scan_buf);
+    launch_i32(fw_phase1_i32<VEC, false>, fw_phase1_i32<VEC, true>, 1, kThreads, s,
+               conv_first | (nb == 1 ? conv_last : 0), scan_buf, d, n, ld, inf, r0);
   else
     hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
   mark(kKindPhase1, false);
@@ -1046,8 +1116,9 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
     mark(kKindPhase2, true);
     if constexpr (std::is_same_v<T, int32_t>)
-      hipLaunchKernelGGL((fw_phase2_i32<VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n,
-                         ld, inf, K, nb, scan_buf);
+      launch_i32(fw_phase2_i32<VEC, false>, fw_phase2_i32<VEC, true>, g2, kP2Threads, s,
+                 (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last : 0), scan_buf, d, n, ld,
+                 inf, K, nb);
     else
       hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n, ld,
                          inf, K, nb);
@@ -1056,8 +1127,9 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     const int fuse = K + 1 < r1 ? 1 : 0;
     mark(kKindPhase3, true);
     if constexpr (std::is_same_v<T, int32_t>)
-      hipLaunchKernelGGL((fw_phase3_i32<VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n,
-                         ld, inf, K, nb, fuse, scan_buf);
+      launch_i32(fw_phase3_i32<VEC, false>, fw_phase3_i32<VEC, true>, g3, kThreads, s,
+                 (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last3 : 0), scan_buf, d, n, ld,
+                 inf, K, nb, fuse);
     else
       hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
                          inf, K, nb, fuse);
@@ -1065,27 +1137,19 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   }
 }
 
-// Scan + conversion around the rounds of an int32 call.
+// The scan that picks the arithmetic of an int32 call, then its rounds.
 template <bool VEC>
 void enqueue_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, int64_t r0, int64_t r1,
                  hipStream_t s, int32_t* scan_buf, PhaseTimer* tm) {
   const int64_t rows = n < kScanBlocks ? n : kScanBlocks;
   if (scan_buf) {
-    if (tm) tm->mark(kKindConvert, true);
+    if (tm) tm->mark(kKindScan, true);
     hipLaunchKernelGGL(scan_zero, dim3(1), dim3(64), 0, s, scan_buf);
     hipLaunchKernelGGL((scan_i32<VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n, ld, inf,
                        scan_buf);
-    hipLaunchKernelGGL((convert_i32<VEC, true>), dim3((unsigned)rows), dim3(kThreads), 0, s, d, n,
-                       ld, inf, scan_buf);
-    if (tm) tm->mark(kKindConvert, false);
+    if (tm) tm->mark(kKindScan, false);
   }
   enqueue_rounds<int32_t, VEC>(d, n, ld, inf, r0, r1, s, scan_buf, tm);
-  if (scan_buf) {
-    if (tm) tm->mark(kKindConvert, true);
-    hipLaunchKernelGGL((convert_i32<VEC, false>), dim3((unsigned)rows), dim3(kThreads), 0, s, d,
-                       n, ld, inf, scan_buf);
-    if (tm) tm->mark(kKindConvert, false);
-  }
 }
 
 // Validates, then enqueues rounds [r0, r1).  For int32 the scan result is
