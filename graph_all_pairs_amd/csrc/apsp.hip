@@ -551,6 +551,16 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
   return g * kBand * m + jp * rows + (ip - base);
 }
 
+// The launch's last, partial wave of tiles.  With R workgroups resident
+// per CU the tiles run in waves of R x CUs; when the tile count leaves a
+// short last wave, that wave would hold the whole launch for one more tile
+// time while most CUs idle.  The host keeps the first `full` tiles whole
+// and hands each remaining tile to four workgroups, one 64 x 64 quarter
+// each (all kB pivots, 4 x 4 accumulators per thread): the dispatcher
+// starts them as the last whole tiles free their slots, and a quarter takes
+// a fraction of a tile's time.  Workgroups b < full take whole tiles,
+// b >= full quarter (b - full) % 4 of tile full + (b - full) / 4.
+//
 // conv: kConvC converts the C tile on load, kConvA / kConvB the pivot
 // column / row operands (which the last round's Phase 2 stored as int32),
 // kConvOut the stores; kConvDiag (last round) has workgroup 0 also convert
@@ -558,30 +568,53 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
 // finished reading.
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
-                                            int64_t K, int64_t nb, int fuse_next,
+                                            int64_t K, int64_t nb, int fuse_next, uint32_t full,
                                             T* __restrict__ lds, int conv, int32_t inf32) {
   const uint32_t m = (uint32_t)(nb - 1);
-  const uint32_t total = m * m;
   const uint32_t b = blockIdx.x;
-  const uint32_t x = b % kXcds, j = b / kXcds;
-  const uint32_t q = total / kXcds, rem = total % kXcds;
-  uint32_t L = x * q + min(x, rem) + j;
   const uint32_t kp = (uint32_t)K;  // tile (K+1, K+1) is (kp, kp) in the skipped grid
+  const int tid = threadIdx.x;
+  const int cin = conv & (kConvC | kConvA | kConvB);
+  const bool cout = (conv & kConvOut) != 0;
+  const int64_t kb0 = K * kB;
+  const uint32_t ls = fuse_next ? p3_encode(kp, kp, m) : 0;
+  if (b >= full) {
+    const uint32_t p = b - full;
+    uint32_t L = full + p / 4;
+    if (fuse_next && L == ls) L = 0;  // tile 0 went to workgroup 0 (full >= 1 then)
+    uint32_t ip, jp;
+    p3_decode(L, m, ip, jp);
+    const int64_t I = ip + (ip >= kp), J = jp + (jp >= kp);
+    const int64_t row0 = I * kB + (p % 4 / 2) * (kB / 2), col0 = J * kB + (p % 2) * (kB / 2);
+    if (row0 >= n || col0 >= n) return;
+    T acc[4][4];
+    if (row0 + kB / 2 <= n && col0 + kB / 2 <= n && kb0 + kB <= n) {
+      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds,
+                                                          acc, 0, kB / kKC, tid, cin, inf32);
+      store_tile<T, kB / 2, kB / 2, 4, 4, VEC, false>(d, n, ld, row0, col0, acc, tid, cout,
+                                                      inf32);
+    } else {
+      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds,
+                                                         acc, 0, kB / kKC, tid, cin, inf32);
+      store_tile<T, kB / 2, kB / 2, 4, 4, VEC, true>(d, n, ld, row0, col0, acc, tid, cout,
+                                                     inf32);
+    }
+    return;
+  }
+  const uint32_t x = b % kXcds, j = b / kXcds;
+  const uint32_t q = full / kXcds, rem = full % kXcds;
+  uint32_t L = x * q + min(x, rem) + j;
   const bool special = fuse_next && L == 0;
   if (fuse_next) {
-    const uint32_t ls = p3_encode(kp, kp, m);
     if (L == 0) L = ls;
     else if (L == ls) L = 0;
   }
   uint32_t ip, jp;
   p3_decode(L, m, ip, jp);
   const int64_t I = ip + (ip >= kp), J = jp + (jp >= kp);
-  const int64_t row0 = I * kB, col0 = J * kB, kb0 = K * kB;
+  const int64_t row0 = I * kB, col0 = J * kB;
 
   T acc[8][8];
-  const int tid = threadIdx.x;
-  const int cin = conv & (kConvC | kConvA | kConvB);
-  const bool cout = (conv & kConvOut) != 0;
   const bool interior = row0 + kB <= n && col0 + kB <= n && kb0 + kB <= n;
   if (interior) {
     minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
@@ -736,9 +769,10 @@ fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb
 
 template <typename T, bool VEC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
-fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next) {
+fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next,
+          uint32_t full) {
   __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
-  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, lds, 0, 0);
+  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
 }
 
 template <bool VEC, bool CONV>
@@ -769,14 +803,14 @@ fw_phase2_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64
 template <bool VEC, bool CONV>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
 fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
-              int fuse_next, int conv, const int32_t* __restrict__ s) {
+              int fuse_next, uint32_t full, int conv, const int32_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP3];
   if (f32_exact(s, n))
     phase3_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
-                            fuse_next, reinterpret_cast<float*>(lds), CONV ? conv : 0,
+                            fuse_next, full, reinterpret_cast<float*>(lds), CONV ? conv : 0,
                             inf);
   else
-    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, lds, 0, 0);
+    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1112,6 +1146,15 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   else
     hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
   mark(kKindPhase1, false);
+  // Phase-3 grid: whole tiles, then the quarters of a short last wave.
+  const int64_t tiles = (nb - 1) * (nb - 1);
+  const int64_t slots = (int64_t)kWavesP3 * device_cus();
+  int64_t whole = tiles;
+  if (tiles % slots != 0 && 4 * (tiles % slots) <= slots) whole = tiles - tiles % slots;
+  // Workgroup 0 takes a whole tile: it closes block (K+1, K+1) after the
+  // update, or converts block (K, K) back in the last round.
+  const uint32_t full3 = (uint32_t)(whole > 0 ? whole : 1);
+  const int64_t g3 = tiles > 0 ? full3 + 4 * (tiles - full3) : 0;
   for (int64_t K = r0; K < r1 && nb > 1; ++K) {
     const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
     mark(kKindPhase2, true);
@@ -1123,16 +1166,15 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
       hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n, ld,
                          inf, K, nb);
     mark(kKindPhase2, false);
-    const int64_t g3 = (nb - 1) * (nb - 1);
     const int fuse = K + 1 < r1 ? 1 : 0;
     mark(kKindPhase3, true);
     if constexpr (std::is_same_v<T, int32_t>)
       launch_i32(fw_phase3_i32<VEC, false>, fw_phase3_i32<VEC, true>, g3, kThreads, s,
                  (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last3 : 0), scan_buf, d, n, ld,
-                 inf, K, nb, fuse);
+                 inf, K, nb, fuse, full3);
     else
       hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
-                         inf, K, nb, fuse);
+                         inf, K, nb, fuse, full3);
     mark(kKindPhase3, false);
   }
 }
