@@ -38,6 +38,53 @@ using namespace apsp_dev;
 constexpr int64_t kMaxBatchedN = 128;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;  // workgroups; more graphs loop
 
+// One quad (row, col .. col+3) of a graph; rows and columns >= n read as
+// inf and are never written.  A quad that straddles column n loads each
+// element from a clamped in-range address and then selects inf, and stores
+// through clamped addresses (an out-of-range element rewrites element n-1 of
+// its row with that element's own value), so a quad costs a branch or two,
+// not one per element: with a branch per element the compiler kept 64 lane
+// masks per thread alive across the closure and spilled them, and the
+// graphs whose n is not a multiple of 8 ran 14 % slower than the next
+// multiple of 8.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void bload4(const T* __restrict__ m, int64_t ld, int64_t n,
+                                       int64_t row, int64_t col, T inf, T (&v)[4]) {
+  if (!EDGE || (row < n && col + 3 < n)) {
+    gload4<T, VEC, false>(m, ld, n, row, col, inf, v);
+    return;
+  }
+  if (row >= n || col >= n) {  // the whole quad is padding
+    v[0] = v[1] = v[2] = v[3] = inf;
+    return;
+  }
+  const T* p = m + row * ld;
+  const int64_t c1 = col + 1 < n ? col + 1 : n - 1, c2 = col + 2 < n ? col + 2 : n - 1;
+  const T x0 = p[col], x1 = p[c1], x2 = p[c2];
+  v[0] = x0;
+  v[1] = col + 1 < n ? x1 : inf;
+  v[2] = col + 2 < n ? x2 : inf;
+  v[3] = inf;  // col + 3 >= n here
+}
+
+// Written with named values rather than a loop over the quad: a loop that
+// indexes the quad made the compiler move it into LDS.
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void bstore4(T* __restrict__ m, int64_t ld, int64_t n, int64_t row,
+                                        int64_t col, const T (&v)[4]) {
+  if (!EDGE || (row < n && col + 3 < n)) {
+    gstore4<T, VEC, false>(m, ld, n, row, col, v);
+    return;
+  }
+  if (row >= n || col >= n) return;
+  const T v0 = v[0], v1 = v[1], v2 = v[2];
+  const T last = col + 2 < n ? v2 : (col + 1 < n ? v1 : v0);  // element n - 1
+  T* p = m + row * ld;
+  p[col] = v0;
+  p[col + 1 < n ? col + 1 : n - 1] = col + 1 < n ? v1 : last;
+  p[col + 2 < n ? col + 2 : n - 1] = col + 2 < n ? v2 : last;
+}
+
 template <int NB, int RT>
 struct BatchShape {
   static constexpr int kThr = NB / RT;          // threads per dimension
@@ -47,13 +94,14 @@ struct BatchShape {
 };
 
 // VEC: 16-byte aligned quads (d, ld and stride all allow it); EDGE: n < NB.
-// The 8 x 8 micro-tile kernels are held to 168 VGPRs (3 waves per SIMD, a
-// few spills outside the pivot loop): measured 10 % faster than the 176
-// registers (2 waves) the compiler picks unconstrained, and faster than 4
-// waves (34-37 spills).
+// Waves per SIMD for the 8 x 8 micro-tile kernels, measured on 8192 graphs:
+// 3 when n is the class edge (fits 168 VGPRs without spills; 4 waves were
+// 1-3 % slower), 4 when n < NB (128 VGPRs, at most 2 spills except 14 for
+// binary32 NB = 64): their boundary loads and stores leave gaps that a
+// fourth wave fills, 3-10 % faster than 3 waves at n = 44, 98, 100, 118.
 template <typename T, int NB, int RT, bool VEC, bool EDGE>
 __global__ void __launch_bounds__((NB / RT) * (NB / RT))
-__attribute__((amdgpu_waves_per_eu(RT == 8 ? 3 : 1)))
+__attribute__((amdgpu_waves_per_eu(RT == 8 ? (EDGE ? 4 : 3) : 1)))
 fw_batched(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stride, T inf) {
   using S = BatchShape<NB, RT>;
   __shared__ __attribute__((aligned(16))) T lds[8 * NB];
@@ -62,15 +110,21 @@ fw_batched(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stri
   for (int64_t g = blockIdx.x; g < batch; g += gridDim.x) {
     T* m = d + g * stride;
     T acc[RT][RT];
+    // The per-element addresses and bounds are recomputed for every graph
+    // (the opaque copies stop the compiler hoisting them out of the graph
+    // loop, where they would stay live across the closure and spill).
+    int tr_l = tr, tc_l = tc;
+    int64_t n_l = n;
+    asm volatile("" : "+v"(tr_l), "+v"(tc_l), "+s"(n_l));
 #pragma unroll
     for (int gi = 0; gi < S::G; ++gi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t row = gi * S::S + tr * 4 + i;
+        const int64_t row = gi * S::S + tr_l * 4 + i;
 #pragma unroll
         for (int gj = 0; gj < S::G; ++gj) {
           T v[4];
-          gload4<T, VEC, EDGE>(m, ld, n, row, gj * S::S + tc * 4, inf, v);
+          bload4<T, VEC, EDGE>(m, ld, n_l, row, gj * S::S + tc_l * 4, inf, v);
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[gi * 4 + i][gj * 4 + j] = v[j];
         }
@@ -78,17 +132,21 @@ fw_batched(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t stri
     // The closure ends with a barrier after its last LDS reads, so the next
     // graph may publish into the buffers right away.
     close_block_t<T, NB, RT>(acc, lds);
+    tr_l = tr;
+    tc_l = tc;
+    n_l = n;
+    asm volatile("" : "+v"(tr_l), "+v"(tc_l), "+s"(n_l));
 #pragma unroll
     for (int gi = 0; gi < S::G; ++gi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t row = gi * S::S + tr * 4 + i;
+        const int64_t row = gi * S::S + tr_l * 4 + i;
 #pragma unroll
         for (int gj = 0; gj < S::G; ++gj) {
           T v[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = acc[gi * 4 + i][gj * 4 + j];
-          gstore4<T, VEC, EDGE>(m, ld, n, row, gj * S::S + tc * 4, v);
+          bstore4<T, VEC, EDGE>(m, ld, n_l, row, gj * S::S + tc_l * 4, v);
         }
       }
   }
