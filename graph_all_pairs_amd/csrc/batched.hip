@@ -177,13 +177,28 @@ fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t
   for (int64_t g = blockIdx.x; g < batch; g += gridDim.x) {
     T* m = d + g * stride;
     T acc[R][R];
+    // As in fw_batched: per-graph copies keep the bounds from being hoisted
+    // out of the graph loop, and out-of-range elements load from a clamped
+    // address and are replaced by inf, with no branch per element.
+    int lr_l = lr, lc_l = lc;
+    int64_t n_l = n;
+    asm volatile("" : "+v"(lr_l), "+v"(lc_l), "+s"(n_l));
 #pragma unroll
     for (int ri = 0; ri < R; ++ri) {
-      const int i = 8 * ri + lr;
-      const T* row = m + (int64_t)i * ld + lc;  // element (i, 8 cj + lc) at row[8 cj]
+      const int i = 8 * ri + lr_l;
+      if constexpr (!EDGE) {
+        const T* row = m + (int64_t)(8 * ri + lr) * ld + lc;  // element (i, 8 cj + lc) at row[8 cj]
 #pragma unroll
-      for (int cj = 0; cj < R; ++cj)
-        acc[ri][cj] = (!EDGE || (i < n && 8 * cj + lc < n)) ? row[8 * cj] : inf;
+        for (int cj = 0; cj < R; ++cj) acc[ri][cj] = row[8 * cj];
+      } else {
+        const T* row = m + (int64_t)(i < n_l ? i : n_l - 1) * ld;
+#pragma unroll
+        for (int cj = 0; cj < R; ++cj) {
+          const int64_t c = 8 * cj + lc_l;
+          const T x = row[c < n_l ? c : n_l - 1];
+          acc[ri][cj] = (i < n_l && c < n_l) ? x : inf;
+        }
+      }
     }
     // Pivots 8 s + owner and 8 s + owner + 1 into buffer buf.
     auto publish = [&](int buf, int owner, auto slot) {
@@ -242,14 +257,15 @@ fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t
     // Recompute the addresses here rather than keep the loads' row pointers
     // live through the closure.
     int lr_s = lr, lc_s = lc;
-    asm volatile("" : "+v"(lr_s), "+v"(lc_s));
+    int64_t n_s = n;
+    asm volatile("" : "+v"(lr_s), "+v"(lc_s), "+s"(n_s));
 #pragma unroll
     for (int ri = 0; ri < R; ++ri) {
       const int i = 8 * ri + lr_s;
       T* row = m + (int64_t)i * ld + lc_s;
 #pragma unroll
       for (int cj = 0; cj < R; ++cj)
-        if (!EDGE || (i < n && 8 * cj + lc_s < n)) row[8 * cj] = acc[ri][cj];
+        if (!EDGE || (i < n_s && 8 * cj + lc_s < n_s)) row[8 * cj] = acc[ri][cj];
     }
   }
 }
