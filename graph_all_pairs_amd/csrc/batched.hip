@@ -185,12 +185,13 @@ fw_batched_wave(T* __restrict__ d, int64_t batch, int64_t n, int64_t ld, int64_t
     asm volatile("" : "+v"(lr_l), "+v"(lc_l), "+s"(n_l));
 #pragma unroll
     for (int ri = 0; ri < R; ++ri) {
-      const int i = 8 * ri + lr_l;
       if constexpr (!EDGE) {
-        const T* row = m + (int64_t)(8 * ri + lr) * ld + lc;  // element (i, 8 cj + lc) at row[8 cj]
+        // element (8 ri + lr, 8 cj + lc) at row[8 cj]
+        const T* row = m + (int64_t)(8 * ri + lr) * ld + lc;
 #pragma unroll
         for (int cj = 0; cj < R; ++cj) acc[ri][cj] = row[8 * cj];
       } else {
+        const int i = 8 * ri + lr_l;
         const T* row = m + (int64_t)(i < n_l ? i : n_l - 1) * ld;
 #pragma unroll
         for (int cj = 0; cj < R; ++cj) {
