@@ -566,7 +566,7 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
 // kConvOut the stores; kConvDiag (last round) has workgroup 0 also convert
 // block (K, K) back, which no Phase-3 workgroup reads and Phase 2 has
 // finished reading.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool PAIR_CLOSE = false>
 __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, int fuse_next, uint32_t full,
                                             T* __restrict__ lds, int conv, int32_t inf32) {
@@ -619,12 +619,18 @@ __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_
   if (interior) {
     minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
                                                 kB / kKC, tid, cin, inf32);
-    if (special) close_block_seq<T>(acc, lds);
+    if (special) {
+      if constexpr (PAIR_CLOSE) close_block<T>(acc, lds);
+      else close_block_seq<T>(acc, lds);
+    }
     store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, row0, col0, acc, tid, cout, inf32);
   } else {
     minplus_update<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
                                                kB / kKC, tid, cin, inf32);
-    if (special) close_block_seq<T>(acc, lds);
+    if (special) {
+      if constexpr (PAIR_CLOSE) close_block<T>(acc, lds);
+      else close_block_seq<T>(acc, lds);
+    }
     store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, row0, col0, acc, tid, cout, inf32);
   }
   if ((conv & kConvDiag) && b == 0) {
@@ -767,12 +773,12 @@ fw_phase2(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb
   phase2_body<T, VEC>(d, n, ld, inf, K, nb, lds, 0, 0);
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool PC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
 fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb, int fuse_next,
           uint32_t full) {
   __shared__ __attribute__((aligned(16))) T lds[kLdsP3];
-  phase3_body<T, VEC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
+  phase3_body<T, VEC, PC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
 }
 
 template <bool VEC, bool CONV>
@@ -800,17 +806,17 @@ fw_phase2_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64
     phase2_body<int32_t, VEC>(d, n, ld, inf, K, nb, lds, 0, 0);
 }
 
-template <bool VEC, bool CONV>
+template <bool VEC, bool CONV, bool PC>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
 fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K, int64_t nb,
               int fuse_next, uint32_t full, int conv, const int32_t* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP3];
   if (f32_exact(s, n))
-    phase3_body<float, VEC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
-                            fuse_next, full, reinterpret_cast<float*>(lds), CONV ? conv : 0,
-                            inf);
+    phase3_body<float, VEC, PC>(reinterpret_cast<float*>(d), n, ld, __builtin_inff(), K, nb,
+                                fuse_next, full, reinterpret_cast<float*>(lds),
+                                CONV ? conv : 0, inf);
   else
-    phase3_body<int32_t, VEC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
+    phase3_body<int32_t, VEC, PC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1155,6 +1161,14 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   // update, or converts block (K, K) back in the last round.
   const uint32_t full3 = (uint32_t)(whole > 0 ? whole : 1);
   const int64_t g3 = tiles > 0 ? full3 + 4 * (tiles - full3) : 0;
+  // Below about one and a half waves of tiles, workgroup 0's update and
+  // closure of the next diagonal block is the longest chain of the launch,
+  // so in binary32 it closes the block two pivots per barrier (measured
+  // 4-7 % faster per launch at n = 2048 and 4096).  Above, the closure is off
+  // the critical path and the kernel with the one-pivot closure keeps the
+  // faster tile loop (the pair-step kernel was 6 % slower at n = 5120); the
+  // int32 body gains nothing from it (its pair-step kernel spills more).
+  const bool pair_close = 2 * tiles < 3 * slots && (!std::is_same_v<T, int32_t> || scan_buf);
   for (int64_t K = r0; K < r1 && nb > 1; ++K) {
     const int64_t g2 = 2 * (nb - 1) * (kB / kP2);
     mark(kKindPhase2, true);
@@ -1168,13 +1182,22 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     mark(kKindPhase2, false);
     const int fuse = K + 1 < r1 ? 1 : 0;
     mark(kKindPhase3, true);
-    if constexpr (std::is_same_v<T, int32_t>)
-      launch_i32(fw_phase3_i32<VEC, false>, fw_phase3_i32<VEC, true>, g3, kThreads, s,
-                 (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last3 : 0), scan_buf, d, n, ld,
-                 inf, K, nb, fuse, full3);
-    else
-      hipLaunchKernelGGL((fw_phase3<T, VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n, ld,
-                         inf, K, nb, fuse, full3);
+    const int mask3 = (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last3 : 0);
+    if constexpr (std::is_same_v<T, int32_t>) {
+      if (pair_close)
+        launch_i32(fw_phase3_i32<VEC, false, true>, fw_phase3_i32<VEC, true, true>, g3, kThreads,
+                   s, mask3, scan_buf, d, n, ld, inf, K, nb, fuse, full3);
+      else
+        launch_i32(fw_phase3_i32<VEC, false, false>, fw_phase3_i32<VEC, true, false>, g3,
+                   kThreads, s, mask3, scan_buf, d, n, ld, inf, K, nb, fuse, full3);
+    } else {
+      if (pair_close)
+        hipLaunchKernelGGL((fw_phase3<T, VEC, true>), dim3((unsigned)g3), dim3(kThreads), 0, s, d,
+                           n, ld, inf, K, nb, fuse, full3);
+      else
+        hipLaunchKernelGGL((fw_phase3<T, VEC, false>), dim3((unsigned)g3), dim3(kThreads), 0, s,
+                           d, n, ld, inf, K, nb, fuse, full3);
+    }
     mark(kKindPhase3, false);
   }
 }
