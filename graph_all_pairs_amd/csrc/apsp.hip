@@ -68,7 +68,8 @@ constexpr int kWavesP3 = 3;    // waves per SIMD targeted by Phase 3 (<= 168 VGP
                                // others wait on LDS (measured faster than two waves
                                // with software-pipelined operand reads)
 constexpr int kWavesP2 = 4;    // waves per SIMD targeted by Phase 2 (<= 128 VGPRs)
-constexpr int kP3PerCu = 2;    // Phase-3 tiles per CU below which int32 calls stay in int32
+constexpr int kP3PerCu = 2;    // Phase-3 tiles per CU below which signed int32 calls prefer int32
+constexpr int kF32MinTiles = 9;  // Phase-3 tiles below which int32 calls stay in int32
 
 // ---------------------------------------------------------------------------
 // Min-plus tile update  C <- min(C, A (x) B)  for one workgroup.
@@ -1250,15 +1251,18 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
     }
   } commit{tm == &trace_tm ? &trace_tm : nullptr};
   if constexpr (std::is_same_v<T, int32_t>) {
-    // Binary32 pays only when Phase 3 keeps two workgroups on every CU (its
-    // double issue rate needs several waves per SIMD); smaller matrices stay in
-    // int32 and skip the scan.  The scan result lives in a few bytes of
-    // stream-ordered scratch; without it the call stays in int32.
+    // Binary32 pays from nine Phase-3 tiles (n > 384) on: measured against
+    // int32 arithmetic, 1.5 % faster per call at n = 512, 7-9 % at n = 1024
+    // to 2048 (there each round waits on workgroup 0's closure, which is
+    // shorter in binary32), and 2 % slower at n = 384, where the scan costs
+    // more than three rounds save.  Smaller matrices stay in int32 and skip
+    // the scan.  The scan result lives in a few bytes of stream-ordered
+    // scratch; without it the call stays in int32.
     int32_t* scan_buf = nullptr;
     const int64_t tiles = (nb - 1) * (nb - 1);
     const int policy = g_int32_arith.load(std::memory_order_relaxed);
     const bool try_f32 = policy == APSP_ARITH_F32_WHEN_EXACT ||
-                         (policy == APSP_ARITH_AUTO && tiles >= (int64_t)kP3PerCu * device_cus());
+                         (policy == APSP_ARITH_AUTO && tiles >= kF32MinTiles);
     if (try_f32) {
       if (fixed_scan_buf) {
         scan_buf = fixed_scan_buf;

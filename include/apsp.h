@@ -436,9 +436,10 @@ int apsp_release_events(void);
 /*
  * Arithmetic policy of int32 calls (process-wide; affects calls made after
  * it is set).  APSP_ARITH_AUTO (default): binary32 when it is exact (see
- * above) and Phase 3 has at least two 128 x 128 tiles per compute unit,
- * since binary32's double issue rate needs several waves per SIMD; otherwise
- * int32.  APSP_ARITH_F32_WHEN_EXACT: binary32 whenever it is exact.
+ * above) and n > 384 (at least nine Phase-3 tiles; below that the scan that
+ * checks exactness costs more than binary32 saves); otherwise int32.  The
+ * negative-weight entry points keep int32 below two Phase-3 tiles per
+ * compute unit.  APSP_ARITH_F32_WHEN_EXACT: binary32 whenever it is exact.
  * APSP_ARITH_INT32: always int32.  Results are identical under every
  * policy.  Returns APSP_ERR_INVALID_VALUE for an unknown mode.
  */

@@ -199,9 +199,14 @@ def test_timed_variant_counts_launches(torch_dev):
     assert arith == 1            # 999 * 100 <= 2^24: binary32 arithmetic
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
     t = torch.from_numpy(w).to(dev)
-    ms, cnt, arith = ga.fw_timed(t, INF)   # auto: too few tiles for binary32
-    assert cnt == [1, nb, nb, 0] and arith == 0
+    ms, cnt, arith = ga.fw_timed(t, INF)   # auto: 49 tiles, binary32 when exact
+    assert cnt == [1, nb, nb, 1] and arith == 1
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+    ws = gg.erdos_renyi(300, 0.05, 1, 100, 5)
+    t = torch.from_numpy(ws).to(dev)
+    ms, cnt, arith = ga.fw_timed(t, INF)   # auto: 4 tiles, too few for the scan to pay
+    assert cnt == [1, 3, 3, 0] and arith == 0
+    assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(ws))
     wf = gg.complete_f32(300, 3)
     tf = torch.from_numpy(wf).to(dev)
     ms, cnt, arith = ga.fw_timed(tf)

@@ -50,7 +50,7 @@ def big_weight(w, seed):
 def test_two_calls_second_smaller_binary32_then_int32(dev, policy):
     print(f"case noalloc: policy {policy}, n 3000 (exact) then n 1031 (weight > 2^24)",
           flush=True)
-    first = gg.complete(3000, 1, 10000, 41)       # exact in binary32; 529 tiles >= 2 per CU
+    first = gg.complete(3000, 1, 10000, 41)       # exact in binary32; 529 Phase-3 tiles
     second = big_weight(gg.erdos_renyi(1031, 0.05, 1, 1000, 42), 43)
     with ga.int32_arith(policy):
         got1 = call(ga.apsp_fw_i32_noalloc, first, dev)
