@@ -407,28 +407,41 @@ __device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ 
   }
 }
 
-// Standalone Phase 1 (first round of a call).  conv: kConvC converts the
-// block on load, kConvOut on store.
+// Standalone Phase 1 (first round of a call): one workgroup of kP1Threads
+// threads, a 4 x 4 micro-tile each (32 x 32 threads over the 128 x 128
+// block), closing the block two pivots per barrier.  It is one workgroup
+// alone on the GPU, so it runs 16 waves rather than the Phase-3 layout's 4:
+// each pivot pair's work spreads over four waves per SIMD.  conv: kConvC
+// converts the block on load, kConvOut on store.
+constexpr int kP1Threads = 1024;
+template <typename T, bool VEC, bool EDGE>
+__device__ __forceinline__ void phase1_wide(T* __restrict__ d, int64_t n, int64_t ld, T inf,
+                                            int64_t base, T* __restrict__ lds, int conv,
+                                            int32_t inf32) {
+  constexpr int kThr = kB / 4;
+  static_assert(kThr * kThr == kP1Threads, "4 x 4 per thread");
+  const int tc = threadIdx.x % kThr, tr = threadIdx.x / kThr;
+  T acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    gload4x<T, VEC, EDGE>(d, ld, n, base + tr * 4 + i, base + tc * 4, inf, acc[i],
+                          conv & kConvC, inf32);
+  close_block_t<T, kB, 4>(acc, lds);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    gstore4x<T, VEC, EDGE>(d, ld, n, base + tr * 4 + i, base + tc * 4, acc[i],
+                           (conv & kConvOut) != 0, inf32);
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, T* __restrict__ lds, int conv,
                                             int32_t inf32) {
   const int64_t base = K * kB;
-  const int tid = threadIdx.x;
-  T acc[8][8];
-  if (base + kB <= n) {
-    load_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, base, base, acc, tid, conv & kConvC,
-                                            inf32);
-    close_block<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, base, base, acc, tid, conv & kConvOut,
-                                             inf32);
-  } else {
-    load_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, base, base, acc, tid, conv & kConvC,
-                                           inf32);
-    close_block<T>(acc, lds);
-    store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, base, base, acc, tid, conv & kConvOut,
-                                            inf32);
-  }
+  if (base + kB <= n)
+    phase1_wide<T, VEC, false>(d, n, ld, inf, base, lds, conv, inf32);
+  else
+    phase1_wide<T, VEC, true>(d, n, ld, inf, base, lds, conv, inf32);
 }
 
 // ---------------------------------------------------------------------------
@@ -761,7 +774,7 @@ __global__ void __launch_bounds__(kThreads) scan_i32(const int32_t* __restrict__
 // between run instances with no conversion code in their loops.
 // ---------------------------------------------------------------------------
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(kThreads) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
+__global__ void __launch_bounds__(kP1Threads) fw_phase1(T* __restrict__ d, int64_t n, int64_t ld,
                                                       T inf, int64_t K) {
   __shared__ __attribute__((aligned(16))) T lds[kLdsClose];
   phase1_body<T, VEC>(d, n, ld, inf, K, lds, 0, 0);
@@ -783,7 +796,7 @@ fw_phase3(T* __restrict__ d, int64_t n, int64_t ld, T inf, int64_t K, int64_t nb
 }
 
 template <bool VEC, bool CONV>
-__global__ void __launch_bounds__(kThreads) fw_phase1_i32(int32_t* __restrict__ d, int64_t n,
+__global__ void __launch_bounds__(kP1Threads) fw_phase1_i32(int32_t* __restrict__ d, int64_t n,
                                                           int64_t ld, int32_t inf, int64_t K,
                                                           int conv,
                                                           const int32_t* __restrict__ s) {
@@ -1148,10 +1161,10 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
   // Phase 1 runs inside the previous round's Phase-3 launch.
   mark(kKindPhase1, true);
   if constexpr (std::is_same_v<T, int32_t>)
-    launch_i32(fw_phase1_i32<VEC, false>, fw_phase1_i32<VEC, true>, 1, kThreads, s,
+    launch_i32(fw_phase1_i32<VEC, false>, fw_phase1_i32<VEC, true>, 1, kP1Threads, s,
                conv_first | (nb == 1 ? conv_last : 0), scan_buf, d, n, ld, inf, r0);
   else
-    hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kThreads), 0, s, d, n, ld, inf, r0);
+    hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kP1Threads), 0, s, d, n, ld, inf, r0);
   mark(kKindPhase1, false);
   // Phase-3 grid: whole tiles, then the quarters of a short last wave.
   const int64_t tiles = (nb - 1) * (nb - 1);
