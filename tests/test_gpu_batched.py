@@ -82,7 +82,7 @@ def test_batched_i32_er_exact(dev, n):
     assert np.array_equal(got, oracle.default().fw_batched_i32(w))
 
 
-@pytest.mark.parametrize("n", [4, 32, 48, 64, 65, 72, 80, 96, 112, 128])
+@pytest.mark.parametrize("n", [4, 32, 45, 48, 64, 65, 72, 80, 96, 99, 101, 112, 126, 128])
 def test_batched_i32_complete_padded_layout(dev, n):
     # ld > n and a gap between graphs; the smallest legal stride too
     print(f"batched i32 complete n={n}", flush=True)
@@ -112,7 +112,7 @@ def test_batched_i32_rings_closed_form(dev):
         assert all(np.array_equal(got[g], want) for g in range(9))
 
 
-@pytest.mark.parametrize("n", [5, 32, 40, 64, 67, 72, 100, 128])
+@pytest.mark.parametrize("n", [5, 32, 40, 45, 64, 67, 72, 99, 100, 126, 128])
 def test_batched_f32_matches_oracle_and_single_entry(dev, n):
     print(f"batched f32 n={n}", flush=True)
     w = gg.complete_f32_batch(13, n, 400 + n)

@@ -254,6 +254,22 @@ def test_int32_policy_forces_int_arithmetic(torch_dev):
     assert arith == 1 and np.array_equal(got, oracle.fw_i32(w))
 
 
+@pytest.mark.parametrize("n,want", [(384, 0), (385, 1), (513, 1)])
+def test_auto_policy_boundary(torch_dev, n, want):
+    """Under the default policy an exact int32 matrix computes in binary32
+    from nine Phase-3 tiles (n > 384) on, and in int32 without the scan
+    below; the result is the oracle's either way."""
+    print(f"case auto policy n={n}", flush=True)
+    torch, dev = torch_dev
+    w = gg.erdos_renyi(n, 0.05, 1, 1000, 70 + n)
+    t = torch.from_numpy(w).to(dev)
+    ms, cnt, arith = ga.fw_timed(t, INF)
+    nb = (n + 127) // 128
+    assert arith == want
+    assert cnt == [1, nb, nb, 1 if want else 0]
+    assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
+
+
 def test_rounds_resume_in_binary32(torch_dev):
     torch, dev = torch_dev
     n = 300
