@@ -912,7 +912,7 @@ def main() -> int:
     value = float(n) ** 3 / (wall / args.steps)
     arith = "f32" if arith_code == 1 else "int32"
     log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms; traced calls: ms/call by kind "
-        f"[phase1, phase2, phase3, int32 scan] "
+        f"[phase1, phase2, phase3, int32 scan and panel conversion] "
         f"{[round(x / n_traced, 3) for x in phase_ms]}, arithmetic {arith}")
 
     # Phase-3 roofline: algorithmic relaxations per launch / mean launch time.
@@ -980,7 +980,7 @@ def main() -> int:
             "int32_arith_policy": args.int32_arith,
             "input_sha256": sha,
         },
-        "ms_per_step_by_kind": dict(zip(["phase1", "phase2", "phase3", "scan"],
+        "ms_per_step_by_kind": dict(zip(["phase1", "phase2", "phase3", "scan_convert"],
                                         [x / n_traced for x in phase_ms])),
         "traced_steps": n_traced,
         "roofline": roofline,

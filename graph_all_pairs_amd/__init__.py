@@ -419,7 +419,7 @@ def fw_rounds(t, r0, r1, inf=None):
 
 def fw_timed(t, inf=None):
     """Like fw, synchronised; returns (ms per kind, launches per kind, arith)
-    with kinds [Phase 1, Phase 2, Phase 3, int32 scan] and arith 1 when the
+    with kinds [Phase 1, Phase 2, Phase 3, int32 scan and conversion] and arith 1 when the
     call computed in binary32."""
     import torch
     kind, p, n, ld, inf, s = _tensor_args(t, inf)

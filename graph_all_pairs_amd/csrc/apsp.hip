@@ -107,7 +107,7 @@ constexpr int kConvC = 1;      // the C tile's loads
 constexpr int kConvA = 2;      // the A operand's loads (Phase 2 column pieces: the piece itself)
 constexpr int kConvB = 4;      // the B operand's loads (Phase 2 row pieces: the piece itself)
 constexpr int kConvOut = 8;    // every store of the launch
-constexpr int kConvDiag = 16;  // Phase 3 of the last round: block (K, K) goes back too
+constexpr int kConvDiag = 16;  // Phase 3: workgroup 0 also converts block (K, K) back
 
 // gload4, converting int32 entries to binary32 when cv is set.  Elements
 // outside the matrix read as inf32, which converts to +infinity.
@@ -575,11 +575,13 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
 // a fraction of a tile's time.  Workgroups b < full take whole tiles,
 // b >= full quarter (b - full) % 4 of tile full + (b - full) / 4.
 //
-// conv: kConvC converts the C tile on load, kConvA / kConvB the pivot
-// column / row operands (which the last round's Phase 2 stored as int32),
-// kConvOut the stores; kConvDiag (last round) has workgroup 0 also convert
-// block (K, K) back, which no Phase-3 workgroup reads and Phase 2 has
-// finished reading.
+// conv: kConvC converts the C tile on load (first round), kConvOut the
+// stores (last round).  The body can also convert its pivot operands
+// (kConvA, kConvB) and, in workgroup 0, send block (K, K) back (kConvDiag);
+// the round schedule no longer asks for those (the last round keeps its
+// pivot row and column in binary32 and converts them after Phase 3), but
+// taking that code out of this shared body made the kernels every other
+// round runs 1.5 % slower, so it stays.
 template <typename T, bool VEC, bool PAIR_CLOSE = false>
 __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, int fuse_next, uint32_t full,
@@ -831,6 +833,26 @@ fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64
                                 CONV ? conv : 0, inf);
   else
     phase3_body<int32_t, VEC, PC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
+}
+
+// After the last round of a binary32 call: round K's pivot row and column
+// (block (K, K) included) back to int32, in place.  That round's Phase 2
+// left them in binary32, so its Phase 3 read its operands without a
+// conversion in the pivot loop, and converted every other block on store.
+// Workgroup r takes matrix row r: the whole row inside the pivot block,
+// else its kB entries in the pivot columns.
+__global__ void __launch_bounds__(kThreads) pivot_panels_to_i32(int32_t* __restrict__ d,
+                                                                int64_t n, int64_t ld,
+                                                                int32_t inf, int64_t K,
+                                                                const int32_t* __restrict__ s) {
+  if (!f32_exact(s, n)) return;
+  const int64_t r = blockIdx.x;
+  const int64_t k0 = K * kB, k1 = k0 + kB < n ? k0 + kB : n;
+  const bool pivot_row = r >= k0 && r < k1;
+  const int64_t c0 = pivot_row ? 0 : k0, c1 = pivot_row ? n : k1;
+  int32_t* row = d + r * ld;
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += kThreads)
+    row[c] = f32_to_i32(__int_as_float(row[c]), inf);
 }
 
 // ---------------------------------------------------------------------------
@@ -1144,16 +1166,18 @@ void launch_i32(K plain, K conv, int64_t grid, int threads, hipStream_t s, int m
 // In binary32 the matrix is converted on the way: round r0 reads every
 // block once before any other access (block (r0, r0) in Phase 1, its pivot
 // row and column in Phase 2, the rest in Phase 3), so those loads convert;
-// round r1 - 1 writes every block once after its last read, so its stores
-// convert, and Phase 3 of that round converts the pivot row and column it
-// reads (Phase 2 stored them as int32) and, in workgroup 0, block (K, K).
+// Phase 3 of round r1 - 1 writes every block outside its pivot row and
+// column once after its last read, so its stores convert; that round's
+// Phase 2 keeps the pivot row and column in binary32 (Phase 3 reads them as
+// operands), and pivot_panels_to_i32 converts them, block (K, K) included,
+// after the last Phase 3.
 template <typename T, bool VEC>
 void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
                     const int32_t* scan_buf, PhaseTimer* tm) {
   const int64_t nb = (n + kB - 1) / kB;
   const int conv_first = scan_buf ? kConvC : 0;
   const int conv_last = scan_buf ? kConvOut : 0;
-  const int conv_last3 = scan_buf ? kConvOut | kConvA | kConvB | kConvDiag : 0;
+
   auto mark = [&](int k, bool before) {
     if (tm) tm->mark(k, before);
   };
@@ -1188,7 +1212,7 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     mark(kKindPhase2, true);
     if constexpr (std::is_same_v<T, int32_t>)
       launch_i32(fw_phase2_i32<VEC, false>, fw_phase2_i32<VEC, true>, g2, kP2Threads, s,
-                 (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last : 0), scan_buf, d, n, ld,
+                 (K == r0 ? conv_first : 0) | 0 /* the last round's panels stay binary32 */, scan_buf, d, n, ld,
                  inf, K, nb);
     else
       hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n, ld,
@@ -1196,7 +1220,7 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
     mark(kKindPhase2, false);
     const int fuse = K + 1 < r1 ? 1 : 0;
     mark(kKindPhase3, true);
-    const int mask3 = (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last3 : 0);
+    const int mask3 = (K == r0 ? conv_first : 0) | (K + 1 == r1 ? conv_last : 0);
     if constexpr (std::is_same_v<T, int32_t>) {
       if (pair_close)
         launch_i32(fw_phase3_i32<VEC, false, true>, fw_phase3_i32<VEC, true, true>, g3, kThreads,
@@ -1213,6 +1237,14 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
                            d, n, ld, inf, K, nb, fuse, full3);
     }
     mark(kKindPhase3, false);
+  }
+  if constexpr (std::is_same_v<T, int32_t>) {
+    if (scan_buf && nb > 1) {
+      mark(kKindScan, true);
+      hipLaunchKernelGGL(pivot_panels_to_i32, dim3((unsigned)n), dim3(kThreads), 0, s, d, n, ld,
+                         inf, r1 - 1, scan_buf);
+      mark(kKindScan, false);
+    }
   }
 }
 

@@ -44,8 +44,8 @@
  * largest finite entry is at most 2^24, every value the recurrence stores is
  * an integer of at most 2^24, so the kernels compute in binary32, which is
  * exact there and twice as fast on gfx950; the first round's loads convert
- * the entries to binary32 and the last round's stores convert them back, in
- * place within the call.  Otherwise they compute in int32.  A scan kernel
+ * the entries to binary32 and the last round's stores (and a short pass over
+ * its pivot row and column) convert them back, in place within the call.  Otherwise they compute in int32.  A scan kernel
  * makes this choice on the device (no host synchronisation), and the
  * results are identical either way (see apsp_set_int32_arith).
  *
@@ -158,9 +158,11 @@ int apsp_fw_rounds_f32(float *d, int64_t n, int64_t ld, float inf,
  *   *arith          1 if the call computed in binary32, 0 if in int32;
  * kinds (arrays of 4): 0 = standalone Phase 1 (first round only),
  * 1 = Phase 2, 2 = Phase 3 (which also carries the next round's Phase 1),
- * 3 = the int32 scan (one group before the rounds; the conversions to and
- * from binary32 ride in the first round's loads and the last round's
- * stores).  Any pointer may be NULL.  Errors as for apsp_fw_i32.
+ * 3 = the int32 scan before the rounds and, when the call computed in
+ * binary32 over more than one block, the conversion of the last round's
+ * pivot row and column back to int32 after them (the other conversions ride
+ * in the first round's loads and the last round's Phase-3 stores).  Any
+ * pointer may be NULL.  Errors as for apsp_fw_i32.
  */
 int apsp_fw_timed_i32(int32_t *d, int64_t n, int64_t ld, int32_t inf, void *stream,
                       double *phase_ms, int64_t *phase_launch, int *arith);

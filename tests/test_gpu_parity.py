@@ -192,15 +192,15 @@ def test_timed_variant_counts_launches(torch_dev):
     nb = (n + 127) // 128
     with ga.int32_arith(ga.APSP_ARITH_F32_WHEN_EXACT):
         ms, cnt, arith = ga.fw_timed(t, INF)
-    # later Phase 1s run inside Phase-3 launches; the scan is one group (the
-    # conversions ride in the first round's loads and the last round's stores)
-    assert cnt == [1, nb, nb, 1]
+    # later Phase 1s run inside Phase-3 launches; kind 3 is the scan before the
+    # rounds and the last pivot row and column's conversion after them
+    assert cnt == [1, nb, nb, 2]
     assert all(x > 0 for x in ms)
     assert arith == 1            # 999 * 100 <= 2^24: binary32 arithmetic
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
     t = torch.from_numpy(w).to(dev)
     ms, cnt, arith = ga.fw_timed(t, INF)   # auto: 49 tiles, binary32 when exact
-    assert cnt == [1, nb, nb, 1] and arith == 1
+    assert cnt == [1, nb, nb, 2] and arith == 1
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
     ws = gg.erdos_renyi(300, 0.05, 1, 100, 5)
     t = torch.from_numpy(ws).to(dev)
@@ -266,7 +266,7 @@ def test_auto_policy_boundary(torch_dev, n, want):
     ms, cnt, arith = ga.fw_timed(t, INF)
     nb = (n + 127) // 128
     assert arith == want
-    assert cnt == [1, nb, nb, 1 if want else 0]
+    assert cnt == [1, nb, nb, 2 if want else 0]
     assert np.array_equal(t.cpu().numpy(), oracle.fw_i32(w))
 
 
