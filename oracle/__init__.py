@@ -19,7 +19,7 @@ Functions mirror the C library:
     vertex with 0-weight edges to every vertex (Bellman-Ford);
   * ``minplus(c, a, b, inf)``: the min-plus product min(c, a (x) b);
   * ``successors(w, d, inf)``: the first-hop matrix of weights w and
-    distances d;
+    distances d; ``successors_rows(w, d, inf, rows)`` the listed rows of it;
   * ``apsp(m, inf)``: the full distance matrix of an int32 or float32 input
     (float32 is widened exactly to binary64 and the result stays binary64).
 """
@@ -78,6 +78,8 @@ def load(path: str = LIB):
     lib.oracle_minplus_f64.restype = None
     lib.oracle_successors_i64.argtypes = [p, p, p, i64, i64, i64]
     lib.oracle_successors_i64.restype = None
+    lib.oracle_successors_rows_i64.argtypes = [p, p, p, i64, p, i64, i64]
+    lib.oracle_successors_rows_i64.restype = None
     lib.oracle_sssp_i32.argtypes = [p, i64, i64, i32, i64, p]
     lib.oracle_sssp_i32.restype = ctypes.c_int
     lib.oracle_sssp_f64.argtypes = [p, i64, i64, ctypes.c_double, i64, p]
@@ -261,6 +263,19 @@ class Oracle:
             self.lib.oracle_successors_i64(ww.ctypes.data, dd.ctypes.data, nxt.ctypes.data, n, n,
                                            int(inf))
         return nxt
+
+    def successors_rows(self, w, d, inf, rows):
+        """Rows `rows` of successors(w, d, inf), without the others (for spot
+        checks of large matrices): an int32 (len(rows), n) array."""
+        dd = np.ascontiguousarray(d, dtype=np.int64)
+        n = dd.shape[0]
+        rr = np.ascontiguousarray(rows, dtype=np.int64)
+        wr = np.ascontiguousarray(np.asarray(w)[rr, :n], dtype=np.int64)
+        out = np.empty((len(rr), n), dtype=np.int32)
+        if len(rr) and n:
+            self.lib.oracle_successors_rows_i64(wr.ctypes.data, dd.ctypes.data, rr.ctypes.data,
+                                                len(rr), out.ctypes.data, n, int(inf))
+        return out
 
     def apsp(self, m: np.ndarray) -> np.ndarray:
         """Full distance matrix: int32 stays int32, float32 becomes float64."""

@@ -373,3 +373,30 @@ void oracle_successors_i64(const int64_t *w, const int64_t *d, int32_t *nxt, int
       nxt[i * ld + j] = (int32_t)arg;
     }
 }
+
+/*
+ * The same definition for listed rows only, for spot checks of large
+ * matrices: row k of nxt_rows is row rows[k] of the successor matrix, from
+ * row k of w_rows (the out-weights of vertex rows[k]) and all of d.  w_rows
+ * and nxt_rows are r x n, d is n x n (leading dimension n).
+ */
+void oracle_successors_rows_i64(const int64_t *w_rows, const int64_t *d, const int64_t *rows,
+                                int64_t r, int32_t *nxt_rows, int64_t n, int64_t inf) {
+  int nt = oracle_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t k = 0; k < r; ++k) {
+    const int64_t i = rows[k];
+    const int64_t *wi = w_rows + k * n;
+    for (int64_t j = 0; j < n; ++j) {
+      if (i == j) { nxt_rows[k * n + j] = (int32_t)i; continue; }
+      int64_t best = 0, arg = -1;
+      for (int64_t u = 0; u < n; ++u) {
+        if (u == i || wi[u] == inf || d[u * n + j] == inf) continue;
+        const int64_t cand = wi[u] + d[u * n + j];
+        if (cand >= inf) continue;
+        if (arg < 0 || cand < best) { best = cand; arg = u; }
+      }
+      nxt_rows[k * n + j] = (int32_t)arg;
+    }
+  }
+}

@@ -578,6 +578,30 @@ def test_successors_are_the_smallest_shortest_first_hop(orc, seed):
                 assert nxt[i, j] == min(hops[i][j])
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_successor_rows_are_the_listed_rows(orc, seed):
+    # the row-restricted form takes the same definition for the listed rows,
+    # in any order and with repeats; checked against brute force on tiny
+    # graphs and against the full matrix on larger ones
+    rng = np.random.default_rng(61000 + seed)
+    n = int(rng.integers(2, 8))
+    w = random_small_graph(rng, n, 0.5, 3, INF)
+    w = np.where((w == 0) & ~np.eye(n, dtype=bool), 1, w)
+    best, hops = all_shortest_first_hops(w, INF)
+    d = orc.fw_i32(w)
+    rows = rng.integers(0, n, size=5)
+    got = orc.successors_rows(w, d, INF, rows)
+    for k, i in enumerate(rows):
+        for j in range(n):
+            want = i if i == j else (-1 if best[i][j] == INF else min(hops[i][j]))
+            assert got[k, j] == want
+    w = gg.erdos_renyi(90, 0.2, 0, 4, 500 + seed)
+    np.fill_diagonal(w, 0)
+    d = orc.fw_i32(w)
+    rows = rng.integers(0, 90, size=7)
+    assert np.array_equal(orc.successors_rows(w, d, INF, rows), orc.successors(w, d, INF)[rows])
+
+
 def test_successors_on_a_grid_closed_form(orc):
     # unit grid, vertex r*C + c: the smallest neighbour index that moves closer
     # is up (r - 1) if the target row is above, else left, else right, else down
