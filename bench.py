@@ -672,16 +672,21 @@ def bench_shard(args) -> int:
 
 
 def bench_paths(args) -> int:
-    """Distances plus successors: a step is one apsp_fw_i32 call and one
-    apsp_successors_i32 call on a dense workload's matrix; the roofline entry
-    is the successor pass (its kernels between HIP events on its stream).
-    Dense weights (more than n^2/16 edges) run an argmin product, bound by
-    the int32 VALU: with packed keys (non-negative weights and distances
-    whose largest finite sum is below inf and 2^(31 - ceil(log2 n))) at 1.5
-    instructions per candidate, like the min-plus product, else at 4 (add,
-    compare, two selects); sparse weights run the neighbour-list kernel, n
-    candidates per edge, each reading 4 bytes of D (bound by memory: reported
-    against HBM, although most reads hit L2 and the MALL)."""
+    """Distances plus successors.  A dense int32 workload whose weights fit the
+    key form (see apsp_fw_paths_i32) runs one apsp_fw_paths_i32 call per
+    step: the rounds on keys value << s | first hop, in int32 arithmetic, with
+    no successor pass; the roofline entry is that call's Phase-3 kernel
+    (fw_keys_phase3), from the launch trace, against the dual-issue VALU rate.
+    Any other workload runs one apsp_fw_i32 and one apsp_successors_i32 call
+    per step (what apsp_fw_paths_i32 does for it); the roofline entry is the
+    successor pass (its kernels between HIP events on its stream).  Dense
+    weights run an argmin product, bound by the int32 VALU: with packed keys
+    (non-negative weights and distances whose largest finite sum is below inf
+    and 2^(31 - ceil(log2 n))) at 1.5 instructions per candidate, like the
+    min-plus product, else at 4 (add, compare, two selects); sparse weights
+    run the neighbour-list kernel, n candidates per edge, each reading 4 bytes
+    of D (bound by memory: reported against HBM, although most reads hit L2
+    and the MALL)."""
     import numpy as np
     import torch
 
@@ -696,12 +701,27 @@ def bench_paths(args) -> int:
     sha = gg.sha256_matrix(w, n)
     log(f"workload {args.workload}: successors of {base}, n={n}")
     tw = torch.from_numpy(w).to(dev)
-    copies = [tw.clone() for _ in range(args.warmup + args.steps)]
+    copies = [tw.clone() for _ in range(1 + args.warmup + args.steps)]
     nxt = torch.empty((n, n), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
+    # Which form the library takes for this matrix: one call on a spare copy.
+    if ga.apsp_fw_paths_i32(copies[0].data_ptr(), n, nxt.data_ptr(), n, n, gg.INF_I32, s) \
+            != ga.APSP_OK:
+        raise RuntimeError("apsp_fw_paths_i32 failed")
+    torch.cuda.synchronize()
+    keys = ga.apsp_fw_paths_last_form() == 1
+    copies = copies[1:]
+    B = ga.apsp_pivot_block(n)
+    nb = (n + B - 1) // B
+
     def step(d, evs=None):
+        if keys:
+            if ga.apsp_fw_paths_i32(d.data_ptr(), n, nxt.data_ptr(), n, n, gg.INF_I32, s) \
+                    != ga.APSP_OK:
+                raise RuntimeError("apsp_fw_paths_i32 failed")
+            return
         if ga.apsp_fw_i32(d.data_ptr(), n, n, gg.INF_I32, s) != ga.APSP_OK:
             raise RuntimeError("apsp_fw_i32 failed")
         if evs:
@@ -715,18 +735,55 @@ def bench_paths(args) -> int:
     for i in range(args.warmup):
         step(copies[i])
     torch.cuda.synchronize()
+    n_traced = min(2, args.steps) if keys else 0
+    launches_per_call = 2 * nb + 8
+    if keys:
+        for _ in range(2):  # create the trace's event pool outside the region
+            if ga.apsp_trace_begin(n_traced * launches_per_call) != ga.APSP_OK:
+                raise RuntimeError("apsp_trace_begin failed")
+            ga.apsp_trace_end()
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     wall0 = time.perf_counter()
     for i in range(args.steps):
+        if keys and i == args.steps - n_traced:
+            st = ga.apsp_trace_begin(n_traced * launches_per_call)
+            if st != ga.APSP_OK:
+                raise ga.APSPError(st, "apsp_trace_begin")
         step(copies[args.warmup + i], evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    succ_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     ms_per_step = 1e3 * wall / args.steps
     edges = int((w[:n, :n] < gg.INF_I32).sum() - np.count_nonzero(np.diag(w[:n, :n]) < gg.INF_I32))
     sparse = edges <= n * n // 16
-    if sparse:
+    succ_ms = None
+    if keys:
+        st, phase_ms, launches, dropped = ga.apsp_trace_end()
+        if st != ga.APSP_OK or dropped:
+            raise RuntimeError(f"launch trace failed: status {st}, {dropped} launches not recorded")
+        p3_relax = sum(phase3_relaxations_per_round(n, B)) * n_traced
+        p3_launch = launches[2]
+        p3_ms_avg = phase_ms[2] / max(p3_launch, 1)
+        relax_per_launch = p3_relax / max(p3_launch, 1)
+        achieved = relax_per_launch / (p3_ms_avg * 1e-3) if p3_ms_avg > 0 else 0.0
+        peak = PEAK_RELAX["int32"]
+        st_c, ceil = ga.apsp_minplus_ceiling(0)
+        roofline = {"bound": "alu", "kernel": "fw_keys_phase3",
+                    "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "Trelax/s",
+                    "frac": achieved / peak,
+                    "traffic": read_traffic(args.workload, relax_per_launch),
+                    "relax_per_launch": relax_per_launch, "avg_launch_ms": p3_ms_avg,
+                    "launches": p3_launch,
+                    "ceiling_measured": ceil / 1e12 if st_c == ga.APSP_OK else None,
+                    "note": "the rounds on successor keys (value << s | first hop) in int32 "
+                            "arithmetic: two VOP3 adds and one v_min3_i32 per pair of pivots, "
+                            "as the int32 Phase 3; peak: the dual-issue VALU rate / 1.5; "
+                            "ceiling_measured: the register-only int32 replica"}
+        log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step, one pass on successor keys; "
+            f"traced ms/call by kind {[round(x / n_traced, 3) for x in phase_ms]}")
+    elif sparse:
+        succ_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
         # Algorithmic HBM bytes: W and D read once, the successor matrix written
         # once.  The kernel loads a D row per edge (4 bytes per candidate); those
         # loads are mostly served by L2 and the last-level cache, so they are
@@ -742,6 +799,7 @@ def bench_paths(args) -> int:
                     "note": "achieved: W and D read once, successors written once (12 n^2 bytes); "
                             "gather_GBps: 4 bytes of D per candidate, n candidates per edge"}
     else:
+        succ_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
         # The library's choice between its two dense kernels, from the same facts.
         d = copies[-1]
         wf, df_ = tw[tw < gg.INF_I32], d[d < gg.INF_I32]
@@ -775,8 +833,9 @@ def bench_paths(args) -> int:
                         "launches": args.steps,
                         "note": "peak: dual-issue VALU rate / 4 instructions per candidate "
                                 "(add, compare, two selects)"}
-    log(f"timed {args.steps} steps: {ms_per_step:.1f} ms/step, successor pass {succ_ms:.2f} ms "
-        f"({'neighbour lists' if sparse else 'dense product'}, {edges} edges)")
+    if not keys:
+        log(f"timed {args.steps} steps: {ms_per_step:.1f} ms/step, successor pass {succ_ms:.2f} ms "
+            f"({'neighbour lists' if sparse else 'dense product'}, {edges} edges)")
     rec = {
         "metric": "APSP distances plus successor matrix, n^3/time",
         "value": float(n) ** 3 / (wall / args.steps),
@@ -785,7 +844,9 @@ def bench_paths(args) -> int:
         "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "int32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n": n, "input_sha256": sha,
-                   "successor_ms": succ_ms, "fw_ms": ms_per_step - succ_ms},
+                   "form": "successor keys, one pass" if keys else "rounds, then successor pass",
+                   "successor_ms": succ_ms,
+                   "fw_ms": None if keys else ms_per_step - succ_ms},
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -62,7 +62,8 @@ EXPORTS = (
     "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
     "apsp_trace_begin", "apsp_trace_end", "apsp_minplus_gemm_i32", "apsp_minplus_gemm_f32",
     "apsp_fw_host_i32", "apsp_fw_host_f32", "apsp_fw_host_plan", "apsp_successors_i32",
-    "apsp_successors_f32", "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_path",
+    "apsp_successors_f32", "apsp_fw_paths_i32", "apsp_fw_paths_f32", "apsp_fw_paths_last_form",
+    "apsp_path",
     "apsp_fw_i32_noalloc", "apsp_release_events",
 )
 
@@ -129,6 +130,7 @@ def load(path: str | None = None):
         "apsp_successors_f32": ([vp, i64, vp, i64, vp, i64, i64, f32, vp], ctypes.c_int),
         "apsp_fw_paths_i32": ([vp, i64, vp, i64, i64, i32, vp], ctypes.c_int),
         "apsp_fw_paths_f32": ([vp, i64, vp, i64, i64, f32, vp], ctypes.c_int),
+        "apsp_fw_paths_last_form": ([], ctypes.c_int),
         "apsp_path": ([vp, i64, i64, i64, i64, vp, i64], i64),
         "apsp_trace_begin": ([i64], ctypes.c_int),
         "apsp_trace_end": ([dp, lp, lp], ctypes.c_int),
@@ -246,6 +248,10 @@ def apsp_fw_paths_i32(d, ld, nxt, ldn, n, inf, stream=0) -> int:
 
 def apsp_fw_paths_f32(d, ld, nxt, ldn, n, inf, stream=0) -> int:
     return load().apsp_fw_paths_f32(d or None, ld, nxt or None, ldn, n, inf, stream or None)
+
+
+def apsp_fw_paths_last_form() -> int:
+    return int(load().apsp_fw_paths_last_form())
 
 
 def apsp_path(nxt_host_ptr, ldn, n, i, j, path_ptr=0, cap=0) -> int:
@@ -547,7 +553,10 @@ def fw_host(t, inf=None, device_bytes=0):
 
 def fw_paths(t, nxt=None, inf=None):
     """In-place APSP of t[:n, :n] plus the successor matrix (int32 (n, n)
-    CUDA tensor, allocated when None); returns nxt."""
+    CUDA tensor, allocated when None); returns nxt.  Dense int32 inputs in
+    range take one pass of the rounds on successor keys (the call then
+    synchronises its stream once); apsp_fw_paths_last_form() tells which
+    form ran."""
     import torch
     kind, p, n, ld, inf, s = _tensor_args(t, inf)
     if nxt is None:

@@ -198,13 +198,15 @@ __device__ __forceinline__ void store_tile(T* __restrict__ d, int64_t n, int64_t
 // Chunks c_begin .. c_begin + c_count - 1 of kKC pivots are applied (all
 // kB pivots by default); tid is the thread's index within the 256 threads
 // that share `lds`.  Ends with a barrier after its last LDS reads.
-template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE>
+// MASK: successor keys; the B operand (pivot rows) is staged with its low
+// bits cleared (AND with km), so each sum keeps A's first hop.
+template <typename T, int TM, int TN, int RM, int RN, bool VEC, bool EDGE, bool MASK = false>
 __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t n, int64_t ld,
                                                T inf, int64_t row0, int64_t col0, int64_t kb0,
                                                T* __restrict__ lds, T (&acc)[RM][RN],
                                                int c_begin = 0, int c_count = kB / kKC,
                                                int tid = threadIdx.x, int conv = 0,
-                                               int32_t inf32 = 0) {
+                                               int32_t inf32 = 0, T km = T(0)) {
   using S = TileShape<T, TM, TN, RM, RN>;
   T* sA = lds;                              // [2][kKC][kLdA]
   T* sB = lds + 2 * kKC * S::kLdA;          // [2][kKC][kLdB]
@@ -252,6 +254,10 @@ __device__ __forceinline__ void minplus_update(const T* __restrict__ d, int64_t 
       const int q = tid + l * kThreads;
       if (S::kQuadsB % kThreads == 0 || q < S::kQuadsB) {
         const int kr = q / (TN / 4), cq = q % (TN / 4);
+        if constexpr (MASK) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gb[l][e] &= km;
+        }
         store4(b + kr * S::kLdB + cq * 4, gb[l]);
       }
     }
@@ -315,9 +321,9 @@ constexpr int kLdsP3 = P3::kLdsElems;
 constexpr int kLdsClose = 8 * kB;  // two pivot columns + two pivot rows, two buffers
 
 // The kB x kB block of a 256-thread workgroup in the Phase-3 layout.
-template <typename T>
-__device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds) {
-  close_block_t<T, kB, 8>(acc, lds);
+template <typename T, bool MASK = false>
+__device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds, T km = T(0)) {
+  close_block_t<T, kB, 8, MASK>(acc, lds, km);
 }
 
 // The same closure one pivot per step (d <- min(d, d[x][t] + d[t][y]), one
@@ -326,8 +332,9 @@ __device__ __forceinline__ void close_block(T (&acc)[8][8], T* __restrict__ lds)
 // itself about 4 % slower (measured at n = 8192, also with the fused path
 // switched off, so the cost lies in the compiled kernel, not in the closure's
 // run time); the fused closure is off the critical path at large n.
-template <typename T>
-__device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ lds) {
+template <typename T, bool MASK = false>
+__device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ lds,
+                                                T km = T(0)) {
   T* colv = lds;            // [2][kB]: column t at every row
   T* rowv = lds + 2 * kB;   // [2][kB]: row t at every column
   const int tc = threadIdx.x % 16;
@@ -343,6 +350,13 @@ __device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ 
   if (tr == 0) {
     T v0[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
     T v1[4] = {acc[0][4], acc[0][5], acc[0][6], acc[0][7]};
+    if constexpr (MASK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] &= km;
+        v1[e] &= km;
+      }
+    }
     store4(&rowv[tc * 4], v0);
     store4(&rowv[64 + tc * 4], v1);
   }
@@ -390,6 +404,13 @@ __device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ 
           if (tr == owner) {
             T v0[4] = {acc[slot][0], acc[slot][1], acc[slot][2], acc[slot][3]};
             T v1[4] = {acc[slot][4], acc[slot][5], acc[slot][6], acc[slot][7]};
+            if constexpr (MASK) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v0[e] &= km;
+                v1[e] &= km;
+              }
+            }
             store4(&rv[tc * 4], v0);
             store4(&rv[64 + tc * 4], v1);
           }
@@ -414,10 +435,10 @@ __device__ __forceinline__ void close_block_seq(T (&acc)[8][8], T* __restrict__ 
 // each pivot pair's work spreads over four waves per SIMD.  conv: kConvC
 // converts the block on load, kConvOut on store.
 constexpr int kP1Threads = 1024;
-template <typename T, bool VEC, bool EDGE>
+template <typename T, bool VEC, bool EDGE, bool MASK = false>
 __device__ __forceinline__ void phase1_wide(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t base, T* __restrict__ lds, int conv,
-                                            int32_t inf32) {
+                                            int32_t inf32, T km = T(0)) {
   constexpr int kThr = kB / 4;
   static_assert(kThr * kThr == kP1Threads, "4 x 4 per thread");
   const int tc = threadIdx.x % kThr, tr = threadIdx.x / kThr;
@@ -426,22 +447,22 @@ __device__ __forceinline__ void phase1_wide(T* __restrict__ d, int64_t n, int64_
   for (int i = 0; i < 4; ++i)
     gload4x<T, VEC, EDGE>(d, ld, n, base + tr * 4 + i, base + tc * 4, inf, acc[i],
                           conv & kConvC, inf32);
-  close_block_t<T, kB, 4>(acc, lds);
+  close_block_t<T, kB, 4, MASK>(acc, lds, km);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     gstore4x<T, VEC, EDGE>(d, ld, n, base + tr * 4 + i, base + tc * 4, acc[i],
                            (conv & kConvOut) != 0, inf32);
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool MASK = false>
 __device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, T* __restrict__ lds, int conv,
-                                            int32_t inf32) {
+                                            int32_t inf32, T km = T(0)) {
   const int64_t base = K * kB;
   if (base + kB <= n)
-    phase1_wide<T, VEC, false>(d, n, ld, inf, base, lds, conv, inf32);
+    phase1_wide<T, VEC, false, MASK>(d, n, ld, inf, base, lds, conv, inf32, km);
   else
-    phase1_wide<T, VEC, true>(d, n, ld, inf, base, lds, conv, inf32);
+    phase1_wide<T, VEC, true, MASK>(d, n, ld, inf, base, lds, conv, inf32, km);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,18 +479,19 @@ __device__ __forceinline__ void phase1_body(T* __restrict__ d, int64_t n, int64_
 // result is the same bit for bit as one half applying all pivots).
 // ---------------------------------------------------------------------------
 constexpr int kP2Threads = 2 * kThreads;
-template <typename T, int TM, int TN, bool VEC, bool EDGE>
+template <typename T, int TM, int TN, bool VEC, bool EDGE, bool MASK = false>
 __device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                           int64_t row0, int64_t col0, int64_t kb0,
-                                          T* __restrict__ lds, int conv, int32_t inf32) {
+                                          T* __restrict__ lds, int conv, int32_t inf32,
+                                          T km = T(0)) {
   using S = TileShape<T, TM, TN, 4, 4>;
   constexpr int kHalf = kB / kKC / 2;  // chunks per half
   const int half = threadIdx.x / kThreads;
   const int tid = threadIdx.x % kThreads;
   T acc[4][4];
-  minplus_update<T, TM, TN, 4, 4, VEC, EDGE>(d, n, ld, inf, row0, col0, kb0,
-                                             lds + half * S::kLdsElems, acc, half * kHalf, kHalf,
-                                             tid, conv, inf32);
+  minplus_update<T, TM, TN, 4, 4, VEC, EDGE, MASK>(d, n, ld, inf, row0, col0, kb0,
+                                                   lds + half * S::kLdsElems, acc, half * kHalf,
+                                                   kHalf, tid, conv, inf32, km);
   // Both halves passed minplus_update's final barrier: the LDS is free.
   constexpr int kLdR = TN + kPad;
   static_assert(TM * kLdR <= 2 * S::kLdsElems, "the hand-over fits the LDS");
@@ -492,23 +514,24 @@ __device__ __forceinline__ void p2_halves(T* __restrict__ d, int64_t n, int64_t 
   }
 }
 
-template <typename T, int TM, int TN, bool VEC>
+template <typename T, int TM, int TN, bool VEC, bool MASK = false>
 __device__ __forceinline__ void p2_piece(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                          int64_t row0, int64_t col0, int64_t kb0,
-                                         T* __restrict__ lds, int conv, int32_t inf32) {
+                                         T* __restrict__ lds, int conv, int32_t inf32,
+                                         T km = T(0)) {
   if (row0 + TM <= n && col0 + TN <= n && kb0 + kB <= n)
-    p2_halves<T, TM, TN, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32);
+    p2_halves<T, TM, TN, VEC, false, MASK>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32, km);
   else
-    p2_halves<T, TM, TN, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32);
+    p2_halves<T, TM, TN, VEC, true, MASK>(d, n, ld, inf, row0, col0, kb0, lds, conv, inf32, km);
 }
 
 // conv: kConvC converts the piece's own entries on load (as C and as its
 // operand: B of a row piece, A of a column piece; D_KK is already binary32),
 // kConvOut converts on store.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool MASK = false>
 __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, T* __restrict__ lds, int conv,
-                                            int32_t inf32) {
+                                            int32_t inf32, T km = T(0)) {
   const int own = (conv & kConvC) ? kConvC : 0;
   constexpr int kSub = kB / kP2;
   const int64_t nr = (nb - 1) * kSub;
@@ -519,16 +542,16 @@ __device__ __forceinline__ void phase2_body(T* __restrict__ d, int64_t n, int64_
     const int64_t J = jp + (jp >= K);
     const int64_t col0 = J * kB + sub * kP2;
     if (col0 >= n) return;
-    p2_piece<T, kB, kP2, VEC>(d, n, ld, inf, kb0, col0, kb0, lds,
-                              own | (own ? kConvB : 0) | (conv & kConvOut), inf32);
+    p2_piece<T, kB, kP2, VEC, MASK>(d, n, ld, inf, kb0, col0, kb0, lds,
+                                    own | (own ? kConvB : 0) | (conv & kConvOut), inf32, km);
   } else {
     b -= nr;
     const int64_t ip = b / kSub, sub = b % kSub;
     const int64_t I = ip + (ip >= K);
     const int64_t row0 = I * kB + sub * kP2;
     if (row0 >= n) return;
-    p2_piece<T, kP2, kB, VEC>(d, n, ld, inf, row0, kb0, kb0, lds,
-                              own | (own ? kConvA : 0) | (conv & kConvOut), inf32);
+    p2_piece<T, kP2, kB, VEC, MASK>(d, n, ld, inf, row0, kb0, kb0, lds,
+                                    own | (own ? kConvA : 0) | (conv & kConvOut), inf32, km);
   }
 }
 
@@ -582,10 +605,11 @@ __device__ __forceinline__ uint32_t p3_encode(uint32_t ip, uint32_t jp, uint32_t
 // pivot row and column in binary32 and converts them after Phase 3), but
 // taking that code out of this shared body made the kernels every other
 // round runs 1.5 % slower, so it stays.
-template <typename T, bool VEC, bool PAIR_CLOSE = false>
+template <typename T, bool VEC, bool PAIR_CLOSE = false, bool MASK = false>
 __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_t ld, T inf,
                                             int64_t K, int64_t nb, int fuse_next, uint32_t full,
-                                            T* __restrict__ lds, int conv, int32_t inf32) {
+                                            T* __restrict__ lds, int conv, int32_t inf32,
+                                            T km = T(0)) {
   const uint32_t m = (uint32_t)(nb - 1);
   const uint32_t b = blockIdx.x;
   const uint32_t kp = (uint32_t)K;  // tile (K+1, K+1) is (kp, kp) in the skipped grid
@@ -605,13 +629,15 @@ __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_
     if (row0 >= n || col0 >= n) return;
     T acc[4][4];
     if (row0 + kB / 2 <= n && col0 + kB / 2 <= n && kb0 + kB <= n) {
-      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds,
-                                                          acc, 0, kB / kKC, tid, cin, inf32);
+      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, false, MASK>(d, n, ld, inf, row0, col0, kb0,
+                                                                lds, acc, 0, kB / kKC, tid, cin,
+                                                                inf32, km);
       store_tile<T, kB / 2, kB / 2, 4, 4, VEC, false>(d, n, ld, row0, col0, acc, tid, cout,
                                                       inf32);
     } else {
-      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds,
-                                                         acc, 0, kB / kKC, tid, cin, inf32);
+      minplus_update<T, kB / 2, kB / 2, 4, 4, VEC, true, MASK>(d, n, ld, inf, row0, col0, kb0,
+                                                               lds, acc, 0, kB / kKC, tid, cin,
+                                                               inf32, km);
       store_tile<T, kB / 2, kB / 2, 4, 4, VEC, true>(d, n, ld, row0, col0, acc, tid, cout,
                                                      inf32);
     }
@@ -633,19 +659,19 @@ __device__ __forceinline__ void phase3_body(T* __restrict__ d, int64_t n, int64_
   T acc[8][8];
   const bool interior = row0 + kB <= n && col0 + kB <= n && kb0 + kB <= n;
   if (interior) {
-    minplus_update<T, kB, kB, 8, 8, VEC, false>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
-                                                kB / kKC, tid, cin, inf32);
+    minplus_update<T, kB, kB, 8, 8, VEC, false, MASK>(d, n, ld, inf, row0, col0, kb0, lds, acc,
+                                                      0, kB / kKC, tid, cin, inf32, km);
     if (special) {
-      if constexpr (PAIR_CLOSE) close_block<T>(acc, lds);
-      else close_block_seq<T>(acc, lds);
+      if constexpr (PAIR_CLOSE) close_block<T, MASK>(acc, lds, km);
+      else close_block_seq<T, MASK>(acc, lds, km);
     }
     store_tile<T, kB, kB, 8, 8, VEC, false>(d, n, ld, row0, col0, acc, tid, cout, inf32);
   } else {
-    minplus_update<T, kB, kB, 8, 8, VEC, true>(d, n, ld, inf, row0, col0, kb0, lds, acc, 0,
-                                               kB / kKC, tid, cin, inf32);
+    minplus_update<T, kB, kB, 8, 8, VEC, true, MASK>(d, n, ld, inf, row0, col0, kb0, lds, acc,
+                                                     0, kB / kKC, tid, cin, inf32, km);
     if (special) {
-      if constexpr (PAIR_CLOSE) close_block<T>(acc, lds);
-      else close_block_seq<T>(acc, lds);
+      if constexpr (PAIR_CLOSE) close_block<T, MASK>(acc, lds, km);
+      else close_block_seq<T, MASK>(acc, lds, km);
     }
     store_tile<T, kB, kB, 8, 8, VEC, true>(d, n, ld, row0, col0, acc, tid, cout, inf32);
   }
@@ -833,6 +859,53 @@ fw_phase3_i32(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64
                                 CONV ? conv : 0, inf);
   else
     phase3_body<int32_t, VEC, PC>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Successor keys: distances and first hops in one pass of the rounds.
+//
+// The matrix holds int32 keys v << s | h, with s the bit width of n (so
+// 2^s > n and h = 2^s - 1 names no vertex) and "no edge" the key
+// 2^30 - 2^s.  For a pivot k the sum (a << s | h) + (b << s) =
+// (a + b) << s | h stands for the walk i -> k -> j with the first hop h of
+// its i -> k part, and the minimum of keys orders by value, then by first
+// hop.  So the blocked recurrence, run unchanged on keys with the low s bits
+// of every pivot-row operand cleared, leaves in each entry the smallest
+// (distance, first hop) over the walks it has seen, which at the end is the
+// shortest distance and the smallest first hop of a shortest path: the
+// successor of the page "Study of Betweenness Centrality Algorithms in GPU"
+// (predecessor arrays), with the same tie rule as the separate successor
+// pass.  Keys stay exact and below 2^31 when every value the recurrence
+// stores is below 2^(30-s) - 1; the caller checks that before choosing
+// this path.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t key_mask(int64_t n) {
+  const int s = 32 - __clz((int)n);  // 1 <= n < 2^29 on this path
+  return (int32_t)(~((1u << s) - 1u));
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kP1Threads) fw_keys_phase1(int32_t* __restrict__ d, int64_t n,
+                                                           int64_t ld, int32_t inf, int64_t K) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsClose];
+  phase1_body<int32_t, VEC, true>(d, n, ld, inf, K, lds, 0, 0, key_mask(n));
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kP2Threads) __attribute__((amdgpu_waves_per_eu(kWavesP2)))
+fw_keys_phase2(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K,
+               int64_t nb) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[2 * kLdsP2];
+  phase2_body<int32_t, VEC, true>(d, n, ld, inf, K, nb, lds, 0, 0, key_mask(n));
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesP3)))
+fw_keys_phase3(int32_t* __restrict__ d, int64_t n, int64_t ld, int32_t inf, int64_t K,
+               int64_t nb, int fuse_next, uint32_t full) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[kLdsP3];
+  phase3_body<int32_t, VEC, false, true>(d, n, ld, inf, K, nb, fuse_next, full, lds, 0, 0,
+                                         key_mask(n));
 }
 
 // After the last round of a binary32 call: round K's pivot row and column
@@ -1171,9 +1244,10 @@ void launch_i32(K plain, K conv, int64_t grid, int threads, hipStream_t s, int m
 // Phase 2 keeps the pivot row and column in binary32 (Phase 3 reads them as
 // operands), and pivot_panels_to_i32 converts them, block (K, K) included,
 // after the last Phase 3.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool KEYS = false>
 void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, hipStream_t s,
                     const int32_t* scan_buf, PhaseTimer* tm) {
+  static_assert(!KEYS || std::is_same_v<T, int32_t>, "successor keys are int32");
   const int64_t nb = (n + kB - 1) / kB;
   const int conv_first = scan_buf ? kConvC : 0;
   const int conv_last = scan_buf ? kConvOut : 0;
@@ -1195,7 +1269,9 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
       launch_i32(fw_phase1_i32<VEC, false>, fw_phase1_i32<VEC, true>, 1, kP1Threads, s,
                  conv_first | (nb == 1 ? conv_last : 0), scan_buf, d, n, ld, inf, r0);
   }
-  if (!dual)
+  if constexpr (KEYS)
+    hipLaunchKernelGGL((fw_keys_phase1<VEC>), dim3(1), dim3(kP1Threads), 0, s, d, n, ld, inf, r0);
+  else if (!dual)
     hipLaunchKernelGGL((fw_phase1<T, VEC>), dim3(1), dim3(kP1Threads), 0, s, d, n, ld, inf, r0);
   mark(kKindPhase1, false);
   // Phase-3 grid: whole tiles, then the quarters of a short last wave.
@@ -1224,7 +1300,10 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
                    K == r0 ? conv_first : 0 /* the last round's panels stay binary32 */, scan_buf,
                    d, n, ld, inf, K, nb);
     }
-    if (!dual)
+    if constexpr (KEYS)
+      hipLaunchKernelGGL((fw_keys_phase2<VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n,
+                         ld, inf, K, nb);
+    else if (!dual)
       hipLaunchKernelGGL((fw_phase2<T, VEC>), dim3((unsigned)g2), dim3(kP2Threads), 0, s, d, n, ld,
                          inf, K, nb);
     mark(kKindPhase2, false);
@@ -1241,7 +1320,10 @@ void enqueue_rounds(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, 
                      kThreads, s, mask3, scan_buf, d, n, ld, inf, K, nb, fuse, full3);
       }
     }
-    if (!dual) {
+    if constexpr (KEYS) {
+      hipLaunchKernelGGL((fw_keys_phase3<VEC>), dim3((unsigned)g3), dim3(kThreads), 0, s, d, n,
+                         ld, inf, K, nb, fuse, full3);
+    } else if (!dual) {
       if (pair_close)
         hipLaunchKernelGGL((fw_phase3<T, VEC, true>), dim3((unsigned)g3), dim3(kThreads), 0, s, d,
                            n, ld, inf, K, nb, fuse, full3);
@@ -1340,6 +1422,31 @@ int run(T* d, int64_t n, int64_t ld, T inf, int64_t r0, int64_t r1, void* stream
     (void)scan_out;
     if (vec) enqueue_rounds<T, true>(d, n, ld, inf, r0, r1, s, nullptr, tm);
     else enqueue_rounds<T, false>(d, n, ld, inf, r0, r1, s, nullptr, tm);
+  }
+  return launch_status();
+}
+
+// Every round on successor keys (see key_mask), in place on s.  The caller
+// has validated the matrix and checked that the keys stay exact.
+int run_keys(int32_t* d, int64_t n, int64_t ld, hipStream_t s) {
+  const int64_t nb = (n + kB - 1) / kB;
+  const int sb = 32 - __builtin_clz((unsigned)n);
+  const int32_t inf_key = (int32_t)((1u << 30) - (1u << sb));
+  PhaseTimer trace_tm;
+  PhaseTimer* tm = nullptr;
+  if (g_trace.on) {
+    trace_tm.ev = g_trace.ev + 2 * g_trace.used;
+    trace_tm.kind = g_trace.kind + g_trace.used;
+    trace_tm.cap = g_trace.cap - g_trace.used;
+    trace_tm.s = s;
+    tm = &trace_tm;
+  }
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(d) % 16 == 0);
+  if (vec) enqueue_rounds<int32_t, true, true>(d, n, ld, inf_key, 0, nb, s, nullptr, tm);
+  else enqueue_rounds<int32_t, false, true>(d, n, ld, inf_key, 0, nb, s, nullptr, tm);
+  if (tm) {
+    g_trace.used += trace_tm.used;
+    g_trace.dropped += trace_tm.dropped;
   }
   return launch_status();
 }
@@ -1547,6 +1654,10 @@ int run_signed_f32(float* d, int64_t n, int64_t ld, float inf, void* stream) {
 
 // Library-internal host helpers for the other translation units.
 int apsp_detail_check_device() { return check_device(); }
+int apsp_detail_fw_keys(int32_t* d, int64_t n, int64_t ld, void* stream) {
+  if (d == nullptr || n < 1 || n >= (int64_t(1) << 29) || ld < n) return APSP_ERR_INVALID_VALUE;
+  return run_keys(d, n, ld, reinterpret_cast<hipStream_t>(stream));
+}
 int apsp_detail_launch_status() { return launch_status(); }
 
 extern "C" {

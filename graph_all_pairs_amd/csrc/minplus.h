@@ -181,8 +181,13 @@ __device__ __forceinline__ void gstore4(T* __restrict__ d, int64_t ld, int64_t n
 // a workgroup of (NB/RT)^2 threads, thread (tr, tc) holding rows and columns
 // g*S + 4*tr + i and g*S + 4*tc + j for g < RT/4, i, j < 4, S = NB/(RT/4).
 // LDS: 8*NB elements.
-template <typename T, int NB, int RT>
-__device__ __forceinline__ void close_block_t(T (&acc)[RT][RT], T* __restrict__ lds) {
+//
+// MASK (int32 successor keys, value << s | first hop): every value taken
+// from a pivot row -- the second operand of a sum -- has its low s bits
+// cleared (AND with km), so a sum keeps the first operand's first hop.
+template <typename T, int NB, int RT, bool MASK = false>
+__device__ __forceinline__ void close_block_t(T (&acc)[RT][RT], T* __restrict__ lds,
+                                              T km = T(0)) {
   static_assert(RT % 4 == 0 && NB % RT == 0, "micro-tile of 4x4 groups");
   constexpr int G = RT / 4;          // 4-wide groups per thread and dimension
   constexpr int S = NB / G;          // distance between a thread's groups
@@ -212,6 +217,10 @@ __device__ __forceinline__ void close_block_t(T (&acc)[RT][RT], T* __restrict__ 
         for (int gj = 0; gj < G; ++gj) {
           T v[4] = {acc[slot + h][4 * gj], acc[slot + h][4 * gj + 1], acc[slot + h][4 * gj + 2],
                     acc[slot + h][4 * gj + 3]};
+          if constexpr (MASK) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] &= km;
+          }
           store4(&base[(2 + h) * NB + gj * S + tc * 4], v);
         }
     }
@@ -245,7 +254,9 @@ __device__ __forceinline__ void close_block_t(T (&acc)[RT][RT], T* __restrict__ 
           for (int j = 0; j < 4; ++j) b1[4 * h + j] = v[j];
         }
         const T d_t_t1 = base[2 * NB + t + 1];  // D[t][t+1]
-        const T d_t1_t = base[t + 1];           // D[t+1][t]
+        T d_t1_t = base[t + 1];                 // D[t+1][t]
+        // D[t+1][t] + D[t][y] forms a pivot-row value (row t+1 after pivot t)
+        if constexpr (MASK) d_t1_t &= km;
 #pragma unroll
         for (int i = 0; i < RT; ++i) a1[i] = mp_min(a1[i], mp_add(a0[i], d_t_t1));
 #pragma unroll

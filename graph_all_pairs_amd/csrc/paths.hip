@@ -640,6 +640,97 @@ int run_successors(const T* w, int64_t ldw, const T* d, int64_t ldd, int32_t* nx
   return st_launch;
 }
 
+// ---------------------------------------------------------------------------
+// Distances and successors in one pass of the rounds (int32, dense).
+//
+// For a dense int32 matrix with weights >= 0, a zero diagonal and a bounded
+// range, the rounds run on keys v << s | h (s the bit width of n): each
+// entry then ends as its shortest distance and the smallest first hop of a
+// shortest path, which is the successor defined above (the smallest u != i
+// with w(i, u) + d(u, j) = d(i, j): every such u starts a shortest walk, and
+// every shortest walk's first hop is such a u).  That replaces the n^3
+// successor product by a split of the keys.  Walks that begin with the
+// diagonal entry carry the hop 2^s - 1, which loses every tie, so a first
+// hop is never i itself.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t key_of(int32_t w, int64_t i, int64_t j, int32_t inf, int sb,
+                                          int32_t none) {
+  const uint32_t hop = i == j ? (1u << sb) - 1u : (uint32_t)j;
+  return w >= inf ? none : (int32_t)(((uint32_t)w << sb) | hop);
+}
+
+// The diagonal's range (into st->dmin, st->dmax), one workgroup.
+__global__ void __launch_bounds__(256) keys_diag(const int32_t* __restrict__ d, int64_t ld,
+                                                 int64_t n, SuccStats* __restrict__ st) {
+  int32_t lo = INT32_MAX, hi = INT32_MIN;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t v = d[i * ld + i];
+    lo = min(lo, v);
+    hi = max(hi, v);
+  }
+  unsigned long long none = 0;
+  block_stats(none, lo, hi);
+  if (threadIdx.x == 0) {
+    st->dmin = lo;
+    st->dmax = hi;
+  }
+}
+
+// Weights to keys in place; "no edge" (>= inf) becomes none = 2^30 - 2^s.
+template <bool VEC>
+__global__ void __launch_bounds__(256) keys_pack(int32_t* __restrict__ d, int64_t ld, int64_t n,
+                                                 int32_t inf, int sb) {
+  const int32_t none = (int32_t)((1u << 30) - (1u << sb));
+  const int64_t quads = VEC ? n / 4 : 0;
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+    int32_t* row = d + i * ld;
+    for (int64_t q = threadIdx.x; q < quads; q += blockDim.x) {
+      int32_t v[4];
+      load4(row + q * 4, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = key_of(v[e], i, q * 4 + e, inf, sb, none);
+      store4(row + q * 4, v);
+    }
+    for (int64_t j = quads * 4 + threadIdx.x; j < n; j += blockDim.x)
+      row[j] = key_of(row[j], i, j, inf, sb, none);
+  }
+}
+
+// Keys to distances (in place) and successors.
+__device__ __forceinline__ void key_split(int32_t k, int64_t i, int64_t j, int32_t inf, int sb,
+                                          int32_t none, int32_t& dist, int32_t& hop) {
+  const int32_t v = k >> sb;
+  const bool reach = k < none && v < inf;
+  dist = reach ? v : inf;
+  hop = i == j ? (int32_t)i : (reach ? (int32_t)(k & (int32_t)((1u << sb) - 1u)) : -1);
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) keys_split(int32_t* __restrict__ d, int64_t ld,
+                                                  int32_t* __restrict__ nxt, int64_t ldn,
+                                                  int64_t n, int32_t inf, int sb) {
+  const int32_t none = (int32_t)((1u << 30) - (1u << sb));
+  const int64_t quads = VEC ? n / 4 : 0;
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+    int32_t* row = d + i * ld;
+    int32_t* out = nxt + i * ldn;
+    for (int64_t q = threadIdx.x; q < quads; q += blockDim.x) {
+      int32_t v[4], h[4];
+      load4(row + q * 4, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key_split(v[e], i, q * 4 + e, inf, sb, none, v[e], h[e]);
+      store4(row + q * 4, v);
+      store4(out + q * 4, h);
+    }
+    for (int64_t j = quads * 4 + threadIdx.x; j < n; j += blockDim.x) {
+      int32_t dv, hv;
+      key_split(row[j], i, j, inf, sb, none, dv, hv);
+      row[j] = dv;
+      out[j] = hv;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" int apsp_fw_i32(int32_t* d, int64_t n, int64_t ld, int32_t inf, void* stream);
@@ -647,10 +738,62 @@ extern "C" int apsp_fw_f32(float* d, int64_t n, int64_t ld, float inf, void* str
 
 namespace {
 
-// Distances in place plus successors: the weights are kept in
-// stream-ordered scratch for the successor pass.
+// Whether the one-pass key form applies to the int32 weights d: they are
+// dense (more than n^2/16 finite off-diagonal entries, where the separate
+// pass would run the n^3 product), none is negative, the diagonal is zero,
+// and every value the rounds can store stays below 2^(30-s) - 1 -- it is
+// at most the largest weight when no off-diagonal entry is inf, else at
+// most n - 1 times it (a shortest path is simple).  Reads the statistics
+// back, so the stream is synchronised once.
+int keys_choice(const int32_t* d, int64_t ld, int64_t n, int32_t inf, hipStream_t s, bool* use) {
+  *use = false;
+  if (n >= (int64_t(1) << 29)) return APSP_OK;
+  const int parts = (int)std::min<int64_t>(n, kStatParts);
+  SuccStats* stats = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&stats), sizeof(SuccStats) * (1 + parts), s) !=
+      hipSuccess) {
+    (void)apsp_detail_launch_status();
+    return APSP_ERR_LAUNCH;
+  }
+  SuccStats* part = stats + 1;
+  if (reinterpret_cast<uintptr_t>(d) % 16 == 0 && ld % 4 == 0)
+    hipLaunchKernelGGL((succ_count<int32_t, true>), dim3(parts), dim3(256), 0, s, d, ld, n, inf,
+                       part);
+  else
+    hipLaunchKernelGGL((succ_count<int32_t, false>), dim3(parts), dim3(256), 0, s, d, ld, n, inf,
+                       part);
+  hipLaunchKernelGGL(succ_fold<false>, dim3(1), dim3(256), 0, s, part, parts, stats, 0ull);
+  hipLaunchKernelGGL(keys_diag, dim3(1), dim3(256), 0, s, d, ld, n, stats);
+  SuccStats h{};
+  int st = apsp_detail_launch_status();
+  if (st == APSP_OK &&
+      (hipMemcpyAsync(&h, stats, sizeof(SuccStats), hipMemcpyDeviceToHost, s) != hipSuccess ||
+       hipStreamSynchronize(s) != hipSuccess)) {
+    (void)apsp_detail_launch_status();
+    st = APSP_ERR_LAUNCH;
+  }
+  (void)hipFreeAsync(stats, s);
+  if (st != APSP_OK) return st;
+  const unsigned long long nn = (unsigned long long)n;
+  const int sb = 32 - __builtin_clz((unsigned)n);
+  const int64_t lim = (int64_t(1) << (30 - sb)) - 1;
+  const int64_t wmax = h.edges ? h.wmax : 0;
+  const int64_t bound = h.edges == nn * (nn - 1) ? wmax : (n - 1) * wmax;
+  *use = h.edges > nn * nn / 16 && (h.edges == 0 || h.wmin >= 0) && h.dmin == 0 &&
+         h.dmax == 0 && bound < lim;
+  return APSP_OK;
+}
+
+// The form the last apsp_fw_paths_i32 call of this thread took: 1 keys, 0 the
+// separate successor pass, -1 none yet (or the call failed before choosing).
+thread_local int g_paths_form = -1;
+
+// Distances in place plus successors.  int32 weights for which the key form
+// applies take one pass of the rounds on keys; otherwise the weights are
+// kept in stream-ordered scratch for the successor pass after the rounds.
 template <typename T>
 int run_fw_paths(T* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n, T inf, void* stream) {
+  if constexpr (std::is_same_v<T, int32_t>) g_paths_form = -1;
   if (n < 0 || !inf_ok<T>(inf)) return APSP_ERR_INVALID_VALUE;
   if (n == 0) return APSP_OK;
   if (!mat_ok<T>(d, n, ld, sizeof(T)) || !mat_ok<int32_t>(nxt, n, ldn, sizeof(int32_t)) ||
@@ -659,6 +802,26 @@ int run_fw_paths(T* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n, T inf, 
   int st = apsp_detail_check_device();
   if (st != APSP_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if constexpr (std::is_same_v<T, int32_t>) {
+    bool use = false;
+    st = keys_choice(d, ld, n, inf, s, &use);
+    if (st != APSP_OK) return st;
+    g_paths_form = use ? 1 : 0;
+    if (use) {
+      const int sb = 32 - __builtin_clz((unsigned)n);
+      const dim3 rows((unsigned)std::min<int64_t>(n, 4096));
+      const bool dv = reinterpret_cast<uintptr_t>(d) % 16 == 0 && ld % 4 == 0;
+      const bool nv = dv && reinterpret_cast<uintptr_t>(nxt) % 16 == 0 && ldn % 4 == 0;
+      if (dv) hipLaunchKernelGGL(keys_pack<true>, rows, dim3(256), 0, s, d, ld, n, inf, sb);
+      else hipLaunchKernelGGL(keys_pack<false>, rows, dim3(256), 0, s, d, ld, n, inf, sb);
+      st = apsp_detail_launch_status();
+      if (st == APSP_OK) st = apsp_detail_fw_keys(d, n, ld, stream);
+      if (st != APSP_OK) return st;
+      if (nv) hipLaunchKernelGGL(keys_split<true>, rows, dim3(256), 0, s, d, ld, nxt, ldn, n, inf, sb);
+      else hipLaunchKernelGGL(keys_split<false>, rows, dim3(256), 0, s, d, ld, nxt, ldn, n, inf, sb);
+      return apsp_detail_launch_status();
+    }
+  }
   const int64_t ldw = (n + 3) & ~int64_t(3);
   T* w = nullptr;
   if (hipMallocAsync(reinterpret_cast<void**>(&w), (size_t)(ldw * n * sizeof(T)), s) != hipSuccess) {
@@ -691,6 +854,8 @@ int apsp_fw_paths_f32(float* d, int64_t ld, int32_t* nxt, int64_t ldn, int64_t n
                       void* stream) {
   return run_fw_paths<float>(d, ld, nxt, ldn, n, inf, stream);
 }
+
+int apsp_fw_paths_last_form(void) { return g_paths_form; }
 
 
 int apsp_successors_i32(const int32_t* w, int64_t ldw, const int32_t* d, int64_t ldd,

@@ -287,14 +287,41 @@ int apsp_successors_f32(const float *w, int64_t ldw, const float *d, int64_t ldd
                         int64_t ldn, int64_t n, float inf, void *stream);
 
 /*
- * Distances and successors in one call: apsp_fw_* in place on d, then
+ * Distances and successors in one call: d in place (the apsp_fw_* result)
+ * and nxt (the apsp_successors_* matrix of the weights d held on entry).
+ * Same preconditions as those two (w[i][i] = 0, int32 entries in [0, inf]).
+ *
+ * int32, one-pass form: when the weights are dense (more than n^2/16 finite
+ * off-diagonal entries), none is negative, the diagonal is zero, and every
+ * value the rounds can store stays below 2^(30-s) - 1 with s the bit width
+ * of n (2^(s-1) <= n < 2^s) -- the largest weight when no off-diagonal
+ * entry is inf, else n - 1 times it -- the rounds run once, in int32
+ * arithmetic, on keys v << s | h: the weight or distance v and the first
+ * hop h (the diagonal carries h = 2^s - 1, "no edge" is 2^30 - 2^s).  A
+ * pivot-row operand enters each sum with its low s bits cleared, so
+ * (a << s | h) + (b << s) is the walk i -> k -> j with the first hop of its
+ * i -> k part, and the minimum of keys picks the shortest distance and,
+ * among shortest paths, the smallest first hop: the same nxt as
+ * apsp_successors_*, with no n^3 successor pass.  Defines: "Katz and
+ * Kider" page, section 4.6 (the rounds); "Study of Betweenness Centrality
+ * Algorithms in GPU" (predecessor arrays).  Deciding reads 24 bytes of
+ * statistics back, so int32 calls synchronise `stream` once.
+ *
+ * Otherwise (and always for float32): apsp_fw_* in place on d, then
  * apsp_successors_* from a copy of the weights kept in n*n elements of
- * stream-ordered scratch.  Asynchronous on `stream`.
+ * stream-ordered scratch, asynchronously on `stream`.
  */
 int apsp_fw_paths_i32(int32_t *d, int64_t ld, int32_t *nxt, int64_t ldn, int64_t n, int32_t inf,
                       void *stream);
 int apsp_fw_paths_f32(float *d, int64_t ld, int32_t *nxt, int64_t ldn, int64_t n, float inf,
                       void *stream);
+
+/*
+ * Diagnostic: the form the calling thread's last apsp_fw_paths_i32 call
+ * took -- 1 the one-pass key form, 0 the rounds followed by the successor
+ * pass, -1 no call yet or the call returned an error before choosing.
+ */
+int apsp_fw_paths_last_form(void);
 
 /*
  * The path i -> j from a successor matrix in HOST memory (copy nxt back

@@ -253,3 +253,133 @@ def test_zero_weight_two_cycle(dev, orc, n, p, scale):
     wf = np.where(w == INF, np.float32(np.inf), w.astype(np.float32)).astype(np.float32)
     df = np.where(d == INF, np.float32(np.inf), d.astype(np.float32)).astype(np.float32)
     assert np.array_equal(gpu_successors(dev, wf, df), want)
+
+
+# ---- one pass of the rounds on successor keys (apsp_fw_paths_i32) ----------
+# Dense int32 weights >= 0 with a zero diagonal and a bounded range take the
+# key form (value << s | first hop); everything else takes the rounds and
+# then the successor pass.  Both must give the oracle's distances and its
+# successor matrix bit for bit; apsp_fw_paths_last_form says which ran.
+
+def gpu_fw_paths(dev, w, inf=INF, ld=None, ldn=None, doff=0, noff=0):
+    """apsp_fw_paths_i32 through the C ABI on w placed with leading dimension
+    ld at element offset doff (nxt: ldn, noff); checks that no byte outside
+    the two n x n blocks changed and returns (d, nxt, form)."""
+    n = w.shape[0]
+    ld = n if ld is None else ld
+    ldn = n if ldn is None else ldn
+    dbuf = torch.full((doff + n * ld + 4,), -7, dtype=torch.int32, device=dev)
+    dv = dbuf[doff:doff + n * ld].view(n, ld)
+    dv[:, :n] = torch.from_numpy(np.ascontiguousarray(w)).to(dev)
+    nbuf = torch.full((noff + n * ldn + 4,), -9, dtype=torch.int32, device=dev)
+    nv = nbuf[noff:noff + n * ldn].view(n, ldn)
+    s = torch.cuda.current_stream().cuda_stream
+    st = ga.apsp_fw_paths_i32(dv.data_ptr(), ld, nv.data_ptr(), ldn, n, inf, s)
+    assert st == ga.APSP_OK, ga.apsp_status_string(st)
+    form = ga.apsp_fw_paths_last_form()
+    hd, hn = dbuf.cpu().numpy(), nbuf.cpu().numpy()
+    d = hd[doff:doff + n * ld].reshape(n, ld)
+    nx = hn[noff:noff + n * ldn].reshape(n, ldn)
+    assert (hd[:doff] == -7).all() and (hd[doff + n * ld:] == -7).all() and (d[:, n:] == -7).all()
+    assert (hn[:noff] == -9).all() and (hn[noff + n * ldn:] == -9).all() and (nx[:, n:] == -9).all()
+    return d[:, :n].copy(), nx[:, :n].copy(), form
+
+
+def check_fw_paths(dev, orc, w, form, inf=INF, **layout):
+    d, nxt, got_form = gpu_fw_paths(dev, w, inf=inf, **layout)
+    assert got_form == form
+    want_d = orc.fw_i32(w)
+    assert np.array_equal(d, want_d)
+    assert np.array_equal(nxt, orc.successors(w, want_d, inf))
+    return d, nxt
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 500, 1031])
+def test_fw_paths_keys_complete_with_ties(dev, orc, n):
+    # weights 1..3 on every pair: many shortest paths per pair, so the
+    # smallest-first-hop rule decides most entries
+    print(f"case fw_paths keys complete n={n}", flush=True)
+    w = gg.complete(n, 1, 3, 900 + n)
+    check_fw_paths(dev, orc, w, 1 if n >= 2 else 0)
+
+
+def test_fw_paths_keys_layouts(dev, orc):
+    # padded leading dimensions, unaligned pointers (scalar loads) and
+    # 16-byte-aligned ones with gaps
+    print("case fw_paths keys layouts", flush=True)
+    w = gg.complete(200, 1, 4, 77)
+    check_fw_paths(dev, orc, w, 1, ld=203, ldn=201, doff=1, noff=3)
+    check_fw_paths(dev, orc, w, 1, ld=204, ldn=208, doff=4, noff=8)
+    check_fw_paths(dev, orc, w, 1, ld=200, ldn=203, doff=0, noff=1)
+
+
+@pytest.mark.parametrize("n", [6, 130, 300])
+def test_fw_paths_keys_zero_weights(dev, orc, n):
+    # weights 0..2 on a complete graph: zero-weight cycles everywhere; the
+    # matrix is still the defined one
+    print(f"case fw_paths keys zero weights n={n}", flush=True)
+    w = gg.complete(n, 0, 2, 40 + n)
+    np.fill_diagonal(w, 0)
+    check_fw_paths(dev, orc, w, 1)
+    # and the dense 2-cycle graph (some off-diagonal entries inf)
+    w = zero_cycle_graph(n, 0.9, 800 + n, 0, n - 2)
+    check_fw_paths(dev, orc, w, 1)
+
+
+@pytest.mark.parametrize("hi,form", [(3, 1), (10000, 0)])
+def test_fw_paths_dense_with_missing_edges(dev, orc, hi, form):
+    # p = 0.5 at n = 300: dense, with inf entries, so the bound is (n - 1)
+    # times the largest weight against 2^(30 - 9) - 1: 897 takes the keys,
+    # 2 990 000 the successor pass
+    print(f"case fw_paths dense p=0.5 weights 1..{hi}", flush=True)
+    w = gg.erdos_renyi(300, 0.5, 1, hi, 61)
+    assert (w == INF).any()
+    check_fw_paths(dev, orc, w, form)
+
+
+def test_fw_paths_keys_range_bound(dev, orc):
+    # n = 100: s = 7, keys exact while every stored value is below
+    # 2^23 - 1 = 8388607; on a complete graph that is the largest weight
+    print("case fw_paths keys range bound", flush=True)
+    lim = (1 << 23) - 1
+    w = gg.complete(100, lim - 1000, lim - 1, 5)
+    w[3, 7] = lim - 1
+    check_fw_paths(dev, orc, w, 1)
+    w[3, 7] = lim
+    check_fw_paths(dev, orc, w, 0)
+
+
+def test_fw_paths_keys_small_sentinel(dev, orc):
+    # inf = 60 with weights 20..40 at p = 0.1 (1409 edges, dense): two hops
+    # already weigh 40 or more, and pairs whose every path weighs 60 or more
+    # are unreachable (distance inf, no first hop)
+    print("case fw_paths keys small sentinel", flush=True)
+    inf = 60
+    w = gg.erdos_renyi(120, 0.1, 20, 40, 19, inf=inf)
+    d, nxt = check_fw_paths(dev, orc, w, 1, inf=inf)
+    assert (d == inf).any() and (nxt == -1).any()
+
+
+def test_fw_paths_other_inputs_take_the_successor_pass(dev, orc):
+    print("case fw_paths fallbacks", flush=True)
+    # sparse weights (at most n^2/16 finite): the neighbour-list pass is cheaper
+    check_fw_paths(dev, orc, gg.erdos_renyi(400, 0.05, 1, 3, 8), 0)
+    # a weight above the range of a complete graph of this size
+    w = gg.complete(3000, 1, 3, 9)
+    w[5, 9] = 1 << 18        # s = 12: the bound is 2^18 - 1
+    check_fw_paths(dev, orc, w, 0)
+
+
+def test_fw_paths_keys_complete_8192(dev, orc):
+    # the complete-8192 workload (weights 1..10000): the key form at full
+    # size, every distance against the oracle and sampled successor rows
+    print("case fw_paths keys complete-8192", flush=True)
+    w = gg.make_workload("complete-8192-i32")
+    n = w.shape[0]
+    d, nxt, form = gpu_fw_paths(dev, w)
+    assert form == 1
+    want_d = orc.fw_i32(w)
+    assert np.array_equal(d, want_d)
+    rows = np.array([0, 1, 127, 128, 4095, 4096, 8063, 8064, 8190, 8191]
+                    + list(np.random.default_rng(3).integers(0, n, size=6)))
+    assert np.array_equal(nxt[rows], orc.successors_rows(w, want_d, INF, rows))
