@@ -748,6 +748,14 @@ namespace {
 int keys_choice(const int32_t* d, int64_t ld, int64_t n, int32_t inf, hipStream_t s, bool* use) {
   *use = false;
   if (n >= (int64_t(1) << 29)) return APSP_OK;
+  // A stream under graph capture cannot be synchronised: keep the form that
+  // decides on the device.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)apsp_detail_launch_status();
+    return APSP_ERR_LAUNCH;
+  }
+  if (cs != hipStreamCaptureStatusNone) return APSP_OK;
   const int parts = (int)std::min<int64_t>(n, kStatParts);
   SuccStats* stats = nullptr;
   if (hipMallocAsync(reinterpret_cast<void**>(&stats), sizeof(SuccStats) * (1 + parts), s) !=

@@ -305,7 +305,8 @@ int apsp_successors_f32(const float *w, int64_t ldw, const float *d, int64_t ldd
  * apsp_successors_*, with no n^3 successor pass.  Defines: "Katz and
  * Kider" page, section 4.6 (the rounds); "Study of Betweenness Centrality
  * Algorithms in GPU" (predecessor arrays).  Deciding reads 24 bytes of
- * statistics back, so int32 calls synchronise `stream` once.
+ * statistics back, so int32 calls synchronise `stream` once (on a stream
+ * under graph capture the call does not, and takes the form below).
  *
  * Otherwise (and always for float32): apsp_fw_* in place on d, then
  * apsp_successors_* from a copy of the weights kept in n*n elements of
