@@ -769,6 +769,7 @@ def bench_paths(args) -> int:
         achieved = relax_per_launch / (p3_ms_avg * 1e-3) if p3_ms_avg > 0 else 0.0
         peak = PEAK_RELAX["int32"]
         st_c, ceil = ga.apsp_minplus_ceiling(0)
+        st_w, at3 = ga.apsp_minplus_ceiling_waves(0, 3)
         roofline = {"bound": "alu", "kernel": "fw_keys_phase3",
                     "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "Trelax/s",
                     "frac": achieved / peak,
@@ -776,6 +777,9 @@ def bench_paths(args) -> int:
                     "relax_per_launch": relax_per_launch, "avg_launch_ms": p3_ms_avg,
                     "launches": p3_launch,
                     "ceiling_measured": ceil / 1e12 if st_c == ga.APSP_OK else None,
+                    "ceiling_at_kernel_occupancy": (
+                        {"waves_per_simd": 3, "value": at3 / 1e12, "frac": achieved / at3}
+                        if st_w == ga.APSP_OK and at3 > 0 else None),
                     "note": "the rounds on successor keys (value << s | first hop) in int32 "
                             "arithmetic: two VOP3 adds and one v_min3_i32 per pair of pivots, "
                             "as the int32 Phase 3; peak: the dual-issue VALU rate / 1.5; "
@@ -1014,6 +1018,14 @@ def main() -> int:
         roofline["ceiling_measured"] = own / 1e12
         roofline["frac_of_ceiling"] = achieved / own
     roofline["ceilings_measured"] = {k: v / 1e12 for k, v in ceilings.items()}
+    # The same replica at the Phase-3 kernels' own occupancy, 3 waves per
+    # SIMD: the double issue pairs waves, so one of three runs single-issue.
+    st_w, at3 = ga.apsp_minplus_ceiling_waves(0 if arith == "int32" else 1, 3)
+    if st_w == ga.APSP_OK and at3 > 0:
+        roofline["ceiling_at_kernel_occupancy"] = {
+            "waves_per_simd": 3, "value": at3 / 1e12, "frac": achieved / at3}
+        log(f"register-only ceiling at 3 waves per SIMD: {at3 / 1e12:.2f} Trelax/s "
+            f"(Phase 3 at {achieved / at3:.2f} of it)")
 
     cpu = None
     if not args.no_cpu_baseline:

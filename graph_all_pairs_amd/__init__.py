@@ -56,7 +56,8 @@ INF_I32 = 0x3FFFFFFF
 EXPORTS = (
     "apsp_fw_i32", "apsp_fw_f32", "apsp_fw_rounds_i32", "apsp_fw_rounds_f32",
     "apsp_fw_timed_i32", "apsp_fw_timed_f32", "apsp_set_int32_arith",
-    "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_pivot_block",
+    "apsp_get_int32_arith", "apsp_minplus_ceiling", "apsp_minplus_ceiling_waves",
+    "apsp_pivot_block",
     "apsp_status_string", "apsp_last_hip_error", "apsp_version",
     "apsp_fw_batched_i32", "apsp_fw_batched_f32", "apsp_johnson_i32",
     "apsp_johnson_timed_i32", "apsp_fw_signed_i32", "apsp_fw_signed_f32",
@@ -143,6 +144,7 @@ def load(path: str | None = None):
         "apsp_release_events": ([], ctypes.c_int),
         "apsp_get_int32_arith": ([], ctypes.c_int),
         "apsp_minplus_ceiling": ([ctypes.c_int, dp], ctypes.c_int),
+        "apsp_minplus_ceiling_waves": ([ctypes.c_int, ctypes.c_int, dp], ctypes.c_int),
         "apsp_pivot_block": ([i64], i64),
         "apsp_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "apsp_last_hip_error": ([], ctypes.c_int),
@@ -345,6 +347,14 @@ def apsp_minplus_ceiling(arith: int):
     """(status, relaxations/s) of the register-only min-plus core."""
     r = ctypes.c_double(0.0)
     st = load().apsp_minplus_ceiling(arith, ctypes.byref(r))
+    return int(st), float(r.value)
+
+
+def apsp_minplus_ceiling_waves(arith: int, waves_per_simd: int):
+    """(status, relaxations/s) of the register-only min-plus core at exactly
+    waves_per_simd waves per SIMD (1 to 4)."""
+    r = ctypes.c_double(0.0)
+    st = load().apsp_minplus_ceiling_waves(arith, waves_per_simd, ctypes.byref(r))
     return int(st), float(r.value)
 
 

@@ -11,7 +11,8 @@
 // reach on this device and clock.  It is reported next to the peak derived
 // from unit counts and clock.  A third mix replicates the successor
 // product's packed keys: two unsigned saturating adds and one unsigned
-// three-input min per pair of candidates.
+// three-input min per pair of candidates.  apsp_minplus_ceiling_waves runs
+// it at one given wave count (1 to 4 per SIMD).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -145,4 +146,16 @@ extern "C" int apsp_minplus_ceiling(int arith, double* relax_per_s) {
   if (relax_per_s == nullptr || arith < 0 || arith > 2) return APSP_ERR_INVALID_VALUE;
   if (arith == 2) return measure_best<uint32_t>(relax_per_s);
   return arith == 1 ? measure_best<float>(relax_per_s) : measure_best<int32_t>(relax_per_s);
+}
+
+// The same replica at a given number of waves per SIMD.  The double rate
+// pairs two waves of a SIMD, so an odd count leaves one wave single-issue:
+// this is the rate a kernel resident at that count can reach.
+extern "C" int apsp_minplus_ceiling_waves(int arith, int waves_per_simd, double* relax_per_s) {
+  if (relax_per_s == nullptr || arith < 0 || arith > 2 || waves_per_simd < 1 ||
+      waves_per_simd > 4)
+    return APSP_ERR_INVALID_VALUE;
+  if (arith == 2) return measure<uint32_t>(waves_per_simd, relax_per_s);
+  return arith == 1 ? measure<float>(waves_per_simd, relax_per_s)
+                    : measure<int32_t>(waves_per_simd, relax_per_s);
 }

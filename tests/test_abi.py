@@ -333,3 +333,9 @@ def test_successor_argument_errors(lib, fn):
                (FAKE, 4, FAKE, 4, 4, 0x40000000)]
     for args in bad:
         assert f(*args, 0) == ga.APSP_ERR_INVALID_VALUE
+
+
+def test_ceiling_at_wave_count_rejects_bad_arguments():
+    # checked before any HIP call
+    for arith, w in ((0, 0), (1, 5), (-1, 2), (3, 2)):
+        assert ga.apsp_minplus_ceiling_waves(arith, w)[0] == ga.APSP_ERR_INVALID_VALUE

@@ -340,6 +340,14 @@ def test_minplus_ceiling_diagnostic(torch_dev):
     st, rf = ga.apsp_minplus_ceiling(1)
     assert st == ga.APSP_OK and 0.5 * 5.24e13 < rf < 2.0 * 5.24e13
     assert ga.apsp_minplus_ceiling(5)[0] == ga.APSP_ERR_INVALID_VALUE
+    # at a given wave count: every count runs, and no count beats twice the
+    # best of the even ones
+    for arith, best in ((0, r32), (1, rf)):
+        for w in (1, 2, 3, 4):
+            st, r = ga.apsp_minplus_ceiling_waves(arith, w)
+            assert st == ga.APSP_OK and 0 < r < 2.0 * best, (arith, w, r)
+    for bad in ((0, 0), (0, 5), (3, 2)):
+        assert ga.apsp_minplus_ceiling_waves(*bad)[0] == ga.APSP_ERR_INVALID_VALUE
 
 
 def test_trace_across_calls_counts_every_launch(torch_dev):
