@@ -294,7 +294,8 @@ def check_fw_paths(dev, orc, w, form, inf=INF, **layout):
     return d, nxt
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 500, 1031])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 500, 1031,
+                               2049, 4100])
 def test_fw_paths_keys_complete_with_ties(dev, orc, n):
     # weights 1..3 on every pair: many shortest paths per pair, so the
     # smallest-first-hop rule decides most entries
